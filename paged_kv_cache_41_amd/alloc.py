@@ -1,0 +1,293 @@
+"""Host block allocator: free list, reference counts, copy-on-write, window trim.
+
+Plain host code.  It decides where each new K/V row goes and which pages must
+be copied first; it never touches K/V data.  Its output is what the kernels
+consume: int32 block tables (-1 where a page was released), raw token-slot
+tables, the slot of every new row and the list of pages to copy.
+
+Semantics follow the page table of the silicon-compiler chapter 15 (section
+"The model"):
+
+* ``append`` takes a fresh page when the new row opens a page (row index a
+  multiple of the page size); otherwise, if the tail page is shared
+  (reference count above one), it takes a fresh page, schedules a whole-page
+  copy of the shared one into it, drops one reference to the shared page and
+  maps the copy in its place (lazy copy-on-write).  A failed allocation raises
+  ``OutOfPages`` and leaves the request unchanged.
+* ``trim(keep_from)`` releases front pages while the page after the last
+  released one ends at or before ``keep_from``, so a page that still holds a
+  needed row stays.  After a decode step at context ``L`` with window ``W``
+  the next step needs rows ``>= L + 1 - W``.
+* ``fork`` shares every page, a partial tail included, adding one reference
+  each; ``release`` drops one reference to each page of the request.
+* a page whose count reaches zero goes back on the free list.
+
+The free list is LIFO by default, handing out page 0 first and reusing the
+page freed last first, as in that chapter, so its printed traces reproduce;
+``policy="fifo"`` gives the deque order of the llm-systems-cookbook notebook
+"PagedAttention block allocator" (section "Block allocator").  ``free_order``
+seeds any initial order (a shuffled placement).
+
+``rewind`` (drop the newest rows, freeing pages that no longer hold any) is
+the lifecycle hook of the tiny-llm page "Paged KV Cache" (Task 2), and
+``pages_needed`` is the page-boundary difference of the mini-sglang page
+(section on paged allocation).
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass
+from typing import Dict, Hashable, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class OutOfPages(RuntimeError):
+    """No free page is left in the pool."""
+
+
+@dataclass
+class AppendPlan:
+    """Where one new row goes, and the copy that must run before it is written."""
+    rid: Hashable
+    row: int                      # logical row index of the new row
+    page: int                     # physical page it goes to
+    offset: int                   # row within the page
+    slot: int                     # page * page_size + offset
+    copy: Optional[Tuple[int, int]] = None   # (shared source page, private target page)
+    new_page: bool = False        # the row opened a fresh page
+
+
+@dataclass
+class StepPlan:
+    """The device operands of one decode step for a batch of requests."""
+    rids: List[Hashable]
+    slots: np.ndarray             # int32 [B]
+    copy_src: np.ndarray          # int32 [C]
+    copy_dst: np.ndarray          # int32 [C]
+    context_lens: np.ndarray      # int32 [B], including the new row
+
+
+class BlockAllocator:
+    """Pages of one pool, with reference counts and a free list."""
+
+    def __init__(self, num_pages: int, policy: str = "lifo",
+                 free_order: Optional[Sequence[int]] = None):
+        if num_pages <= 0:
+            raise ValueError("a pool needs at least one page")
+        if policy not in ("lifo", "fifo"):
+            raise ValueError(policy)
+        self.num_pages = num_pages
+        self.policy = policy
+        self.ref = [0] * num_pages
+        order = list(free_order) if free_order is not None else list(range(num_pages))
+        if sorted(order) != list(range(num_pages)):
+            raise ValueError("free_order must be a permutation of the pages")
+        # the next page handed out is order[0] under both policies
+        self._free = deque(order) if policy == "fifo" else list(reversed(order))
+
+    @property
+    def free(self) -> List[int]:
+        return list(self._free)
+
+    def free_count(self) -> int:
+        return len(self._free)
+
+    def used(self) -> int:
+        return self.num_pages - len(self._free)
+
+    def alloc(self) -> int:
+        if not self._free:
+            raise OutOfPages("no free page")
+        p = self._free.popleft() if self.policy == "fifo" else self._free.pop()
+        self.ref[p] = 1
+        return p
+
+    def incref(self, p: int) -> None:
+        if self.ref[p] <= 0:
+            raise ValueError(f"page {p} is not held")
+        self.ref[p] += 1
+
+    def unref(self, p: int) -> None:
+        if self.ref[p] <= 0:
+            raise ValueError(f"page {p} is not held")
+        self.ref[p] -= 1
+        if self.ref[p] == 0:
+            self._free.append(p)
+
+
+class PagedKVCache:
+    """Per-request block tables over one ``BlockAllocator``."""
+
+    def __init__(self, num_pages: int, page_size: int, policy: str = "lifo",
+                 free_order: Optional[Sequence[int]] = None):
+        if page_size <= 0:
+            raise ValueError("page_size must be positive")
+        self.page_size = page_size
+        self.pool = BlockAllocator(num_pages, policy, free_order)
+        self.pages: Dict[Hashable, List[int]] = {}    # live pages, oldest first
+        self.length: Dict[Hashable, int] = {}
+        self.dropped: Dict[Hashable, int] = {}        # front pages released by trim
+
+    # -- lifecycle -------------------------------------------------------------
+    def new(self, rid: Hashable) -> None:
+        if rid in self.pages:
+            raise KeyError(f"request {rid!r} exists")
+        self.pages[rid] = []
+        self.length[rid] = 0
+        self.dropped[rid] = 0
+
+    def append(self, rid: Hashable) -> AppendPlan:
+        """Place one new row at the end of request ``rid``."""
+        P = self.page_size
+        row = self.length[rid]
+        off = row % P
+        pages = self.pages[rid]
+        plan_copy = None
+        new_page = False
+        if off == 0:
+            pages.append(self.pool.alloc())
+            new_page = True
+        else:
+            tail = pages[-1]
+            if self.pool.ref[tail] > 1:
+                fresh = self.pool.alloc()
+                self.pool.unref(tail)
+                pages[-1] = fresh
+                plan_copy = (tail, fresh)
+        page = pages[-1]
+        self.length[rid] = row + 1
+        return AppendPlan(rid, row, page, off, page * P + off, plan_copy, new_page)
+
+    def trim(self, rid: Hashable, keep_from: int) -> List[int]:
+        """Release front pages lying wholly before row ``keep_from``; returns them."""
+        P = self.page_size
+        pages = self.pages[rid]
+        out = []
+        while pages and (self.dropped[rid] + 1) * P <= keep_from:
+            p = pages.pop(0)
+            self.pool.unref(p)
+            self.dropped[rid] += 1
+            out.append(p)
+        return out
+
+    def fork(self, src: Hashable, dst: Hashable) -> None:
+        if dst in self.pages:
+            raise KeyError(f"request {dst!r} exists")
+        self.pages[dst] = list(self.pages[src])
+        self.length[dst] = self.length[src]
+        self.dropped[dst] = self.dropped[src]
+        for p in self.pages[dst]:
+            self.pool.incref(p)
+
+    def release(self, rid: Hashable) -> None:
+        for p in self.pages.pop(rid):
+            self.pool.unref(p)
+        del self.length[rid]
+        del self.dropped[rid]
+
+    def rewind(self, rid: Hashable, n: int) -> List[int]:
+        """Drop the newest ``n`` rows; pages left without a row are released."""
+        if not 0 <= n <= self.length[rid]:
+            raise ValueError("cannot rewind past the start")
+        P = self.page_size
+        new_len = self.length[rid] - n
+        keep = -(-new_len // P) - self.dropped[rid]
+        if keep < 0:
+            raise ValueError("cannot rewind into released pages")
+        pages = self.pages[rid]
+        out = []
+        while len(pages) > keep:
+            p = pages.pop()
+            self.pool.unref(p)
+            out.append(p)
+        self.length[rid] = new_len
+        return out
+
+    # -- queries -----------------------------------------------------------------
+    def used(self) -> int:
+        return self.pool.used()
+
+    def translate(self, rid: Hashable, row: int) -> Tuple[int, int]:
+        """(physical page, offset) of a readable logical row."""
+        P = self.page_size
+        if not self.dropped[rid] * P <= row < self.length[rid]:
+            raise IndexError(f"row {row} of request {rid!r} is not readable")
+        return self.pages[rid][row // P - self.dropped[rid]], row % P
+
+    def table(self, rid: Hashable) -> List[int]:
+        """Block table indexed by logical page; -1 for released pages."""
+        return [-1] * self.dropped[rid] + list(self.pages[rid])
+
+    @staticmethod
+    def pages_needed(cached_len: int, device_len: int, page_size: int) -> int:
+        """Fresh pages to grow a request from ``cached_len`` to ``device_len`` rows."""
+        return -(-device_len // page_size) - (-(-cached_len // page_size))
+
+    # -- device operands ---------------------------------------------------------
+    def block_tables(self, rids: Iterable[Hashable], stride: int) -> np.ndarray:
+        rids = list(rids)
+        out = np.full((len(rids), stride), -1, dtype=np.int32)
+        for i, rid in enumerate(rids):
+            t = self.table(rid)
+            if len(t) > stride:
+                raise ValueError(f"request {rid!r} needs {len(t)} table entries > {stride}")
+            out[i, :len(t)] = t
+        return out
+
+    def slot_table(self, rids: Iterable[Hashable], stride: int, dummy_slot: int) -> np.ndarray:
+        """Raw token-slot table: entry ``[i, r]`` is the flat slot of row ``r``.
+
+        Rows that are not readable, and one extra dummy row at the end, hold
+        ``dummy_slot``.
+        """
+        rids = list(rids)
+        P = self.page_size
+        out = np.full((len(rids) + 1, stride), dummy_slot, dtype=np.int64)
+        for i, rid in enumerate(rids):
+            L = self.length[rid]
+            if L > stride:
+                raise ValueError(f"request {rid!r} has {L} rows > {stride}")
+            d = self.dropped[rid]
+            for j, p in enumerate(self.pages[rid]):
+                r0 = (d + j) * P
+                r1 = min(r0 + P, L)
+                out[i, r0:r1] = p * P + np.arange(r1 - r0)
+        if out.max(initial=0) >= 2**31:
+            raise ValueError("slot does not fit int32")
+        return out.astype(np.int32)
+
+    def plan_step(self, rids: Iterable[Hashable]) -> StepPlan:
+        """Append one row to every request; returns slots and copy lists.
+
+        All-or-nothing: if any append runs out of pages, the appends already
+        made in this call are rewound and ``OutOfPages`` propagates.
+        """
+        rids = list(rids)
+        plans: List[AppendPlan] = []
+        try:
+            for rid in rids:
+                plans.append(self.append(rid))
+        except OutOfPages:
+            for p in reversed(plans):
+                self._undo(p)
+            raise
+        copies = [p.copy for p in plans if p.copy is not None]
+        return StepPlan(
+            rids=rids,
+            slots=np.array([p.slot for p in plans], dtype=np.int32),
+            copy_src=np.array([c[0] for c in copies], dtype=np.int32),
+            copy_dst=np.array([c[1] for c in copies], dtype=np.int32),
+            context_lens=np.array([self.length[r] for r in rids], dtype=np.int32))
+
+    def _undo(self, plan: AppendPlan) -> None:
+        rid = plan.rid
+        pages = self.pages[rid]
+        self.length[rid] = plan.row
+        if plan.new_page:
+            self.pool.unref(pages.pop())
+        elif plan.copy is not None:
+            src, dst = plan.copy
+            self.pool.incref(src)
+            pages[-1] = src
+            self.pool.unref(dst)

@@ -1,0 +1,275 @@
+"""Checks that pin the oracle to things other than itself.
+
+Each ``pin_*`` returns a list of problems (empty: pass), in the style of the
+page checks of the silicon-compiler chapter 15 (section "Tests").  They are
+run by ``test_oracle_pins.py`` and, against deliberately broken copies of the
+oracle, by ``test_oracle_mutants.py``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from helpers import bits, expected_step, ints, table_view
+
+TOL = 1e-11
+
+
+def brute_attention(q_rows, k_rows, v_rows, scale, q_heads, kv_heads):
+    """Scalar-loop attention with correctly rounded sums (math.fsum).
+
+    q_rows ``[Hq][D]``, k_rows/v_rows ``[n][Hkv][D]`` nested lists of floats.
+    Independent of the oracle: no NumPy, no table, no gather.
+    """
+    G = q_heads // kv_heads
+    out = []
+    for h in range(q_heads):
+        g = h // G
+        z = [scale * math.fsum(a * b for a, b in zip(q_rows[h], k[g])) for k in k_rows]
+        m = max(z)
+        w = [math.exp(x - m) for x in z]
+        den = math.fsum(w)
+        D = len(q_rows[h])
+        out.append([math.fsum(w[i] * v_rows[i][g][d] for i in range(len(w))) / den
+                    for d in range(D)])
+    return out
+
+
+def _src_lists(sc, s, lo_rows=None):
+    k = sc.k_src[s].to(torch.float64)
+    v = sc.v_src[s].to(torch.float64)
+    if lo_rows is not None:
+        k, v = k[lo_rows:], v[lo_rows:]
+    return k.tolist(), v.tolist()
+
+
+def _small_scenarios():
+    out = [workloads.make_config(1, keep_source=True)]
+    for seed in (3, 5, 8, 13):
+        out.append(workloads.build(workloads.random_spec(seed), seed, keep_source=True))
+    out.append(workloads.build(workloads.Spec(
+        name="prefix_small", dtype="bf16", num_seqs=5, q_heads=8, kv_heads=2, head_dim=16,
+        page_size=4, prefix_len=12, suffix_lo=0, suffix_hi=9, sibling_cow=True,
+        pool_factor=1.5), 77, keep_source=True))
+    out.append(workloads.build(workloads.Spec(
+        name="slot_small", dtype="bf16", num_seqs=4, q_heads=4, kv_heads=2, head_dim=16,
+        page_size=4, len_dist="lognormal", len_lo=12, len_hi=48, sigma=1.0, slot_table=True,
+        pool_factor=1.25), 91, keep_source=True))
+    return out
+
+
+def pin_bruteforce():
+    """Paged result == scalar attention over the unpaged rows the generator kept."""
+    P = []
+    for sc in _small_scenarios():
+        _, _, out = expected_step(sc)
+        qf = sc.q.to(torch.float64)
+        for s in range(sc.spec.num_seqs):
+            if sc.lens[s] == 0:
+                if np.any(out[s] != 0):
+                    P.append(f"{sc.spec.name} seq {s}: empty context must give zeros")
+                continue
+            k, v = _src_lists(sc, s)
+            ref = np.array(brute_attention(qf[s].tolist(), k, v, sc.scale,
+                                           sc.spec.q_heads, sc.spec.kv_heads))
+            err = float(np.max(np.abs(ref - out[s])))
+            if not err <= TOL:
+                P.append(f"{sc.spec.name} seq {s}: paged oracle vs brute force {err:.3g}")
+    return P
+
+
+def pin_sdpa():
+    """Paged result == torch's scaled_dot_product_attention (float64, GQA) on the unpaged rows."""
+    P = []
+    for sc in _small_scenarios():
+        _, _, out = expected_step(sc)
+        for s in range(sc.spec.num_seqs):
+            if sc.lens[s] == 0:
+                continue
+            q = sc.q[s].to(torch.float64)[None, :, None, :]
+            k = sc.k_src[s].to(torch.float64).permute(1, 0, 2)[None].contiguous()
+            v = sc.v_src[s].to(torch.float64).permute(1, 0, 2)[None].contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, k, v, scale=sc.scale, enable_gqa=True)[0, :, 0, :].numpy()
+            err = float(np.max(np.abs(ref - out[s])))
+            if not err <= TOL:
+                P.append(f"{sc.spec.name} seq {s}: paged oracle vs SDPA {err:.3g}")
+    return P
+
+
+def _hand_pool(rng, n_pages, P, Hkv, D):
+    return rng.standard_normal((n_pages, P, Hkv, D)).astype(np.float32).view(np.uint32)
+
+
+def pin_closed_forms():
+    """L = 1 gives the one value row; equal keys or q = 0 give the mean of the
+    value rows; adding one vector to every key changes nothing."""
+    P = []
+    rng = np.random.default_rng(7)
+    Pg, Hkv, Hq, D = 4, 2, 6, 8
+    kp = _hand_pool(rng, 6, Pg, Hkv, D)
+    vp = _hand_pool(rng, 6, Pg, Hkv, D)
+    table = np.array([[4, 1, 5, 0, -1]])
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32).view(np.uint32)
+    dec = lambda k, v, qq, L, W=0: oracle.attention.decode(
+        qq, k, v, table, np.array([L]), Pg, W, 0.3, "f32")[0]
+    vf = vp.view(np.float32).astype(np.float64)
+    kf = kp.view(np.float32)
+    G = Hq // Hkv
+    # L = 1: the only attended row is logical row 0 = page 4, offset 0
+    o = dec(kp, vp, q, 1)
+    for h in range(Hq):
+        if not np.array_equal(o[h], vf[4, 0, h // G]):
+            P.append("L=1 must return the single value row")
+            break
+    # W = 1 at any L: only the newest row, logical row L-1 = 13 -> logical
+    # page 3 -> physical page 0, offset 1
+    o = dec(kp, vp, q, 14, W=1)
+    if not np.array_equal(o[0], vf[0, 1, 0]):
+        P.append("W=1 must return the newest value row")
+    # equal keys: mean of the value rows, rows 0..10 in table order
+    keq = kf.copy()
+    keq[...] = kf[4, 0][None, None]
+    o = dec(keq.view(np.uint32), vp, q, 11)
+    rows = [vf[table[0, i // Pg], i % Pg] for i in range(11)]
+    mean = np.mean(np.stack(rows), axis=0)
+    for h in range(Hq):
+        if np.max(np.abs(o[h] - mean[h // G])) > 1e-13:
+            P.append("equal keys must give the mean of the value rows")
+            break
+    # q = 0: the mean as well
+    o = dec(kp, vp, np.zeros_like(q), 11)
+    for h in range(Hq):
+        if np.max(np.abs(o[h] - mean[h // G])) > 1e-13:
+            P.append("q = 0 must give the mean of the value rows")
+            break
+    # a common shift of every key: adding c to every key component adds
+    # scale * c * sum(q_h) to every logit of head h, which the softmax ignores.
+    # Keys are multiples of 1/8 so that the shifted keys are exact in float32.
+    kd = (rng.integers(-16, 16, kf.shape) / 8).astype(np.float32)
+    o1 = dec(kd.view(np.uint32), vp, q, 15)
+    o2 = dec((kd + np.float32(0.5)).view(np.uint32), vp, q, 15)
+    if np.max(np.abs(o1 - o2)) > 1e-12:
+        P.append("a common shift of every key changed the output")
+    return P
+
+
+def pin_window():
+    """W >= L equals no window exactly; a window equals attention over exactly
+    the last W unpaged rows; W = 3 is really applied."""
+    P = []
+    spec = workloads.Spec(name="win", dtype="bf16", num_seqs=5, q_heads=4, kv_heads=2,
+                          head_dim=16, page_size=4, lens=(1, 3, 9, 16, 23), pool_factor=1.25)
+    sc = workloads.build(spec, 11, keep_source=True)
+    kp, vp, full = expected_step(sc)
+    args = (bits(sc.q), kp, vp, ints(sc.block_tables), ints(sc.context_lens), 4)
+    qf = sc.q.to(torch.float64)
+    for W in (23, 40):
+        o = oracle.attention.decode(*args, W, sc.scale, "bf16")
+        if not np.array_equal(o, full):
+            P.append(f"a window W={W} >= every L changed the result")
+    for W in (1, 2, 3, 5, 8):
+        o = oracle.attention.decode(*args, W, sc.scale, "bf16")
+        for s in range(5):
+            L = int(sc.lens[s])
+            k, v = _src_lists(sc, s, lo_rows=L - min(L, W))
+            ref = np.array(brute_attention(qf[s].tolist(), k, v, sc.scale, 4, 2))
+            if not np.max(np.abs(ref - o[s])) <= TOL:
+                P.append(f"W={W} seq {s}: differs from attention over the last {W} rows")
+    o3 = oracle.attention.decode(*args, 3, sc.scale, "bf16")
+    if np.max(np.abs(o3[3:] - full[3:])) < 1e-3:
+        P.append("a window of 3 made no difference: it is not applied")
+    return P
+
+
+def pin_placement():
+    """Moving pages to other physical places (and the table with them) changes nothing."""
+    P = []
+    for sc in _small_scenarios():
+        if sc.table_page_size != sc.spec.page_size:
+            continue
+        kp, vp, out = expected_step(sc)
+        n = kp.shape[0]
+        perm = np.random.default_rng(sc.seed + 1).permutation(n)
+        kq = np.empty_like(kp)
+        vq = np.empty_like(vp)
+        kq[perm] = kp
+        vq[perm] = vp
+        bt = ints(sc.block_tables)
+        bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
+        o2 = oracle.attention.decode(bits(sc.q), kq, vq, bt2, ints(sc.context_lens),
+                                     sc.spec.page_size, sc.spec.window, sc.scale, sc.spec.dtype)
+        if not np.array_equal(o2, out):
+            P.append(f"{sc.spec.name}: physical placement changed the output")
+    return P
+
+
+def pin_slot_table():
+    """A raw token-slot table over the flattened pool equals the page table it came from."""
+    P = []
+    sc = _small_scenarios()[-1]
+    assert sc.spec.slot_table
+    kp, vp, out = expected_step(sc)
+    Pg = sc.spec.page_size
+    slot = ints(sc.block_tables)
+    B = sc.spec.num_seqs
+    n_pages = int(np.max(sc.lens + Pg - 1) // Pg)
+    bt = np.full((B, n_pages), -1)
+    for s in range(B):
+        for j in range(-(-int(sc.lens[s]) // Pg)):
+            bt[s, j] = slot[s, j * Pg] // Pg
+    o2 = oracle.attention.decode(bits(sc.q), kp, vp, bt, ints(sc.context_lens), Pg,
+                                 sc.spec.window, sc.scale, sc.spec.dtype)
+    if not np.array_equal(o2, out):
+        P.append("slot table and page table over the same pool differ")
+    return P
+
+
+def pin_store():
+    """After the store, the flattened pool holds each new row at its slot, a
+    negative slot writes nothing, and no other row changed."""
+    P = []
+    rng = np.random.default_rng(5)
+    for dt, npdt in (("bf16", np.uint16), ("f32", np.uint32)):
+        kp = rng.integers(0, 2**16 if dt == "bf16" else 2**32, (7, 3, 2, 4), dtype=np.uint64).astype(npdt)
+        vp = rng.integers(0, 2**16 if dt == "bf16" else 2**32, (7, 3, 2, 4), dtype=np.uint64).astype(npdt)
+        slots = np.array([20, -1, 0, 11, 5])
+        kn = rng.integers(0, 2**15, (5, 2, 4)).astype(npdt)
+        vn = rng.integers(0, 2**15, (5, 2, 4)).astype(npdt)
+        k2, v2 = oracle.kvstore.store_kv(kp, vp, kn, vn, slots)
+        fk, fv, f0 = k2.reshape(21, 2, 4), v2.reshape(21, 2, 4), kp.reshape(21, 2, 4)
+        for t, s in enumerate(slots):
+            if s >= 0 and not (np.array_equal(fk[s], kn[t]) and np.array_equal(fv[s], vn[t])):
+                P.append(f"{dt}: row {t} not at slot {s}")
+        changed = sorted(set(np.nonzero(np.any(fk != f0, axis=(1, 2)))[0].tolist()))
+        if not set(changed) <= {20, 0, 11, 5}:
+            P.append(f"{dt}: rows outside the slots changed: {changed}")
+        if not np.array_equal(np.delete(fv, [20, 0, 11, 5], axis=0),
+                              np.delete(vp.reshape(21, 2, 4), [20, 0, 11, 5], axis=0)):
+            P.append(f"{dt}: value rows outside the slots changed")
+    return P
+
+
+def pin_copy():
+    """Each target page holds the bits of its source; every other page is unchanged."""
+    P = []
+    rng = np.random.default_rng(9)
+    kp = rng.integers(0, 2**16, (9, 4, 2, 4)).astype(np.uint16)
+    vp = rng.integers(0, 2**16, (9, 4, 2, 4)).astype(np.uint16)
+    src, dst = np.array([2, 7, 2]), np.array([5, 0, 8])
+    k2, v2 = oracle.kvstore.copy_pages(kp, vp, src, dst)
+    for s, d in zip(src, dst):
+        if not (np.array_equal(k2[d], kp[s]) and np.array_equal(v2[d], vp[s])):
+            P.append(f"page {d} is not a copy of page {s}")
+    rest = [p for p in range(9) if p not in dst]
+    if not (np.array_equal(k2[rest], kp[rest]) and np.array_equal(v2[rest], vp[rest])):
+        P.append("a page that is not a target changed")
+    return P
+
+
+ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_window, pin_placement,
+            pin_slot_table, pin_store, pin_copy]

@@ -1,0 +1,98 @@
+"""Plant one-line mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+This is the mutation method of the silicon-compiler chapter 15 (section
+"Mutation tests") applied to the oracle: a pin set that lets a plausible
+mistake through is not pinning anything.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from oracle import attention as A
+from oracle import kvstore as S
+
+_live, _gather, _head, _attend = A.live_rows, A.gather, A.kv_head_of, A.attend
+_store, _copy = S.store_kv, S.copy_pages
+
+
+def _gather_shift_page(pool, table_row, lo, hi, dtype):
+    # the page lookup ignores the logical page index offset by one
+    return _gather(pool, np.concatenate([table_row[1:], table_row[:1]]), lo, hi, dtype)
+
+
+def _gather_bad_offset(pool, table_row, lo, hi, dtype):
+    P = pool.shape[1]
+    out = _gather(pool, table_row, lo, hi, dtype)
+    if P > 1 and hi - lo > 1:
+        out = out.copy()
+        out[1:] = out[:-1].copy()       # every row read one slot early
+    return out
+
+
+def _attend_no_norm(q, K, V, scale):
+    z = scale * (K @ q)
+    w = np.exp(z - z.max())
+    return w @ V
+
+
+def _attend_keys(q, K, V, scale):
+    return _attend(q, K, K, scale)
+
+
+def _attend_no_scale(q, K, V, scale):
+    return _attend(q, K, V, 1.0)
+
+
+def _store_off_by_one(k, v, kn, vn, slots):
+    return _store(k, v, kn, vn, np.where(np.asarray(slots) >= 0, np.asarray(slots) + 1, -1) % (k.shape[0] * k.shape[1]))
+
+
+def _store_k_into_v(k, v, kn, vn, slots):
+    return _store(k, v, kn, kn, slots)
+
+
+def _copy_empty(k, v, src, dst):
+    return k.copy(), v.copy()
+
+
+def _copy_keys_only(k, v, src, dst):
+    k2, _ = _copy(k, v, src, dst)
+    return k2, v.copy()
+
+
+MUTANTS = {
+    "gather starts one row late": (A, "live_rows", lambda L, W: (min(_live(L, W)[0] + 1, L), L)),
+    "window keeps W+1 rows": (A, "live_rows", lambda L, W: _live(L, W + 1 if W > 0 else 0)),
+    "window ignored": (A, "live_rows", lambda L, W: (0, L)),
+    "last row dropped": (A, "live_rows", lambda L, W: (_live(L, W)[0], max(L - 1, _live(L, W)[0]))),
+    "page lookup off by one": (A, "gather", _gather_shift_page),
+    "row offset off by one": (A, "gather", _gather_bad_offset),
+    "GQA heads interleaved": (A, "kv_head_of", lambda h, hq, hkv: h % hkv),
+    "softmax not normalised": (A, "attend", _attend_no_norm),
+    "keys where values belong": (A, "attend", _attend_keys),
+    "scale dropped": (A, "attend", _attend_no_scale),
+    "store one slot late": (S, "store_kv", _store_off_by_one),
+    "store writes K into V": (S, "store_kv", _store_k_into_v),
+    "copy-on-write copy is empty": (S, "copy_pages", _copy_empty),
+    "copy forgets V": (S, "copy_pages", _copy_keys_only),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_caught(name, monkeypatch):
+    mod, attr, fn = MUTANTS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            problems = pin()
+        except Exception as e:          # a crash is a catch too
+            problems = [repr(e)]
+        if problems:
+            caught.append(pin.__name__)
+    assert caught, f"mutant '{name}' survived every pin"
+
+
+def test_unbroken_oracle_passes():
+    assert all(pin() == [] for pin in pins.ALL_PINS)
