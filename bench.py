@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step over a paged K/V cache on one MI355X.
+
+A step is the whole path over one batch: page copies for copy-on-write, the
+scatter of the new K/V rows, and paged decode attention (split + merge), all
+through the C ABI on one stream, with every input resident in HBM.  The
+default workload is the batch-64 GQA decode (32 q / 8 kv heads, head_dim 128,
+pages of 16 rows, context lengths uniform in [1, 4096], bf16).
+
+Prints one JSON line: effective KV GB/s of the step (attended K/V bytes per
+step / step time), the decode launch's own time and its fraction of HBM peak
+from HIP events on the launch stream, and the CPU oracle timed on a bounded
+sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--flush", action="store_true",
+                   help="overwrite a 512 MiB buffer before each step (outside the events)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", type=str, default=None,
+                   help="JSON file with measured HBM bytes per decode launch")
+    return p.parse_args()
+
+
+def decode_bytes(sc) -> dict:
+    """Algorithmic bytes of one decode launch and of the attended K/V alone."""
+    import numpy as np
+    s = sc.spec
+    elt = 4 if s.dtype == "f32" else 2
+    n = sc.lens - sc.lo
+    kv = int((2 * n * s.kv_heads * s.head_dim * elt).sum())
+    tps = sc.table_page_size
+    first = sc.lo // tps
+    last = np.where(sc.lens > 0, (sc.lens - 1) // tps, first - 1)
+    table = int((4 * (last - first + 1)).clip(min=0).sum())
+    q = s.num_seqs * s.q_heads * s.head_dim * elt
+    out = s.num_seqs * s.q_heads * s.head_dim * 4
+    return {"kv": kv, "total": kv + table + q + out + 4 * s.num_seqs,
+            "unique_kv": None}
+
+
+def unique_kv_bytes(sc) -> int:
+    """K/V bytes of distinct physical rows attended (differs from kv when pages are shared)."""
+    import numpy as np
+    s = sc.spec
+    elt = 4 if s.dtype == "f32" else 2
+    bt = sc.block_tables.cpu().numpy()
+    seen = set()
+    P = sc.table_page_size
+    for i in range(s.num_seqs):
+        for r in range(int(sc.lo[i]), int(sc.lens[i]), P):
+            seen.add(int(bt[i, r // P]))
+    rows_per = P if P > 1 else 1
+    # rows of each distinct page that some sequence attends (approximate at page grain)
+    return len(seen) * rows_per * 2 * s.kv_heads * s.head_dim * elt
+
+
+def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
+    """The oracle, single-threaded, over whole sequences of the batch until ~budget_s."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    def bits(t):
+        t = t.detach().cpu()
+        return (t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16
+                else t.view(torch.int32).numpy().view(np.uint32))
+
+    s = sc.spec
+    tps = sc.table_page_size
+    kp, vp = bits(sc.k_pool), bits(sc.v_pool)
+    n_, P = kp.shape[:2]
+    kp = kp.reshape(n_ * P // tps, tps, *kp.shape[2:])
+    vp = vp.reshape(n_ * P // tps, tps, *vp.shape[2:])
+    q = bits(sc.q)
+    bt = sc.block_tables.cpu().numpy().astype(np.int64)
+    ctx = sc.context_lens.cpu().numpy().astype(np.int64)
+    elt = 4 if s.dtype == "f32" else 2
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    done, kv_bytes, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s:
+            i = done % s.num_seqs
+            oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype, seqs=[i])
+            kv_bytes += int(2 * (sc.lens[i] - sc.lo[i]) * s.kv_heads * s.head_dim * elt)
+            done += 1
+    dt = time.perf_counter() - t0
+    torch.set_num_threads(torch_threads)
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seqs_per_s": round(done / dt, 3),
+            "sample": f"{done} sequences of this batch in order (cycling), fp64 gather + dense "
+                      f"attention, {dt:.1f} s on 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_cache_41_amd import ops
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc = workloads.make_config(args.config, seed=args.seed, device="cuda:0")
+    s = sc.spec
+    hkv, d = s.kv_heads, s.head_dim
+    kv_view = (sc.k_pool, sc.v_pool) if sc.table_page_size == s.page_size else (
+        sc.k_pool.view(-1, 1, hkv, d), sc.v_pool.view(-1, 1, hkv, d))
+    out = torch.empty(s.num_seqs, s.q_heads, d, dtype=torch.float32, device=dev)
+    need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
+                                      sc.context_lens, window=s.window,
+                                      max_context_len=sc.max_context_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ops.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
+        ops.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+
+    def attend():
+        ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
+                   window=s.window, scale=sc.scale, max_context_len=sc.max_context_len,
+                   out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+        attend()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    wall = 0.0
+    if flush is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step()
+            ev[i][0].record(stream)
+            attend()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        for i in range(args.steps):
+            flush.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step()
+            ev[i][0].record(stream)
+            attend()
+            ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = wall / args.steps * 1e3
+    nb = decode_bytes(sc)
+    dec_avg = float(dec_ms.mean())
+    achieved = nb["total"] / (dec_avg * 1e-3) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(s.name)
+    result = {
+        "metric": "paged decode attention effective KV GB/s (% HBM peak) + seqs/s",
+        "value": round(nb["kv"] / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": s.name, "num_seqs": s.num_seqs, "q_heads": s.q_heads,
+                   "kv_heads": s.kv_heads, "head_dim": s.head_dim, "page_size": s.page_size,
+                   "window": s.window, "seed": sc.seed, "context_sum": int(sc.lens.sum()),
+                   "kv_bytes_per_step": nb["kv"], "copies": int(len(sc.copy_src)),
+                   "stored_rows": int((sc.slot_mapping >= 0).sum()),
+                   "flush_between_steps": bool(args.flush)},
+        "seqs_per_s": round(s.num_seqs / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * nb["kv"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "decode": {"avg_us": round(dec_avg * 1e3, 2), "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                   "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                   "kv_gbps": round(nb["kv"] / (dec_avg * 1e-3) / 1e9, 1),
+                   "seqs_per_s": round(s.num_seqs / (dec_avg * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (split + merge launches)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": nb["total"]},
+    }
+    if s.prefix_len:
+        result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sc)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

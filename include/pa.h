@@ -1,0 +1,133 @@
+/*
+ * pa.h -- C ABI of the paged K/V cache kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations make up one decode step over a paged K/V cache:
+ *
+ *   pa_copy_pages  whole-page copies that implement copy-on-write of shared
+ *                  pages (silicon-compiler chapter 15 "A Paged KV Cache and
+ *                  Sliding-Window Attention", section "The model": before a
+ *                  request writes into a page that others also hold, it copies
+ *                  the page and writes into its own copy);
+ *   pa_store_kv    the scatter of each step's new K/V rows into their slots
+ *                  (mini-sglang part 4, the sections on the KV buffer and its
+ *                  store: the pool is viewed as token rows and a slot list
+ *                  indexes that view);
+ *   pa_decode      single-query attention of every sequence over its rows,
+ *                  reached through a per-sequence block table, optionally
+ *                  limited to the last W rows (silicon chapter 15, sections
+ *                  "The problem" and "The model"; the dense result it must
+ *                  equal is the checkpoint of the tiny-llm page "Paged KV
+ *                  Cache", section "Correctness Checkpoint").
+ *
+ * Common conventions
+ *   - Pools: one K pool and one V pool, each [num_pages, page_size, kv_heads,
+ *     head_dim], row-major, of element type `dtype`.  A "slot" is a row of the
+ *     flattened view [num_pages * page_size, kv_heads, head_dim]:
+ *     slot = page * page_size + offset.  For more than one layer, pass each
+ *     layer's base pointers.
+ *   - dtype: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16, upper half of a
+ *     binary32).  q, new rows and pools share one dtype; decode output is fp32.
+ *   - Every pointer argument is caller-owned device memory unless stated.
+ *     The library allocates nothing, keeps no state between calls, never
+ *     synchronizes, and enqueues all work on `stream` (a hipStream_t; NULL is
+ *     the default stream).  Results are valid after stream-ordered completion.
+ *     Calls are thread-safe.
+ *   - Host-visible arguments are validated and a negative status is returned
+ *     without launching anything.  Device-resident index data (tables, slots,
+ *     copy lists, context lengths) is not validated on the host, since that
+ *     would need a synchronization; the kernels skip any index that falls
+ *     outside the pool instead of accessing it, so a bad index yields wrong
+ *     numbers, never an out-of-bounds access.
+ *   - Alignment: pointers must be aligned to their element size; 16-byte
+ *     aligned pools and rows take the vectorized paths.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 };
+
+enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* a null pointer, a non-positive size, inconsistent sizes  */
+  PA_EUNSUPPORTED = -2,  /* a valid combination this build has no kernel for         */
+  PA_EWORKSPACE = -3,    /* decode workspace missing or smaller than required        */
+  PA_ELAUNCH = -4        /* the HIP runtime rejected a launch                         */
+};
+
+/* Human-readable name of a status code; never NULL. */
+const char* pa_status_string(int status);
+
+/*
+ * pa_store_kv -- write new K/V rows into their slots.
+ *   k_pool, v_pool  [num_pages, page_size, kv_heads, head_dim], written in place.
+ *   k_new, v_new    [num_tokens, kv_heads, head_dim], contiguous.
+ *   slot_mapping    device int32 [num_tokens]: flat slot of each row; a negative
+ *                   slot skips that row.  Slots must be distinct within a call
+ *                   (two rows for one slot: unspecified which one lands).
+ * Every element of each row is copied bit for bit; no other byte of the pools
+ * changes.  num_tokens == 0 is a no-op.
+ */
+int pa_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_pages,
+                int32_t page_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                void* stream);
+
+/*
+ * pa_copy_pages -- pool[dst_pages[i]] = pool[src_pages[i]] for K and V, whole pages.
+ *   src_pages, dst_pages  device int32 [num_copies].  Targets must be distinct and
+ *                         disjoint from the sources, so the order does not matter.
+ * Bit-exact; num_copies == 0 is a no-op.
+ */
+int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_pages,
+                  const int32_t* dst_pages, int32_t num_copies, int32_t num_pages,
+                  int32_t page_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                  void* stream);
+
+/*
+ * pa_decode -- one query token per sequence against its cached rows.
+ *   out           fp32 [num_seqs, q_heads, head_dim], written.
+ *   q             [num_seqs, q_heads, head_dim], pool dtype.
+ *   block_tables  device int32 [num_seqs, bt_stride] (rows beyond num_seqs are
+ *                 ignored): entry j is the physical page of logical page j, or
+ *                 -1 for a page released by the window.  Logical row i lives at
+ *                 page block_tables[s][i / page_size], offset i % page_size.
+ *                 A raw token-slot table is the same call with page_size = 1
+ *                 and num_pages counted in rows.
+ *   context_lens  device int32 [num_seqs]: rows of each sequence, including the
+ *                 token being decoded, whose K/V row must already be stored.
+ *                 0 gives a zero output row.
+ *   window        <= 0: attend rows [0, L); W > 0: rows [L - min(L, W), L).
+ *   max_context_len  host upper bound on every context length; <= 0 means
+ *                 bt_stride * page_size.  Sizes the workspace and the grid;
+ *                 a longer context length is clamped to it.
+ *   scale         logit scale (for instance 1/sqrt(head_dim)).
+ *   q_heads must be a multiple of kv_heads; query head h reads kv head
+ *   h / (q_heads / kv_heads).
+ *   Output: out[s][h] = sum_i softmax_i(scale * <q[s][h], K_i>) * V_i over the
+ *   attended rows, with fp32 accumulation.
+ *   workspace     device scratch of *workspace_bytes bytes.  With workspace ==
+ *                 NULL the call only stores the required size in
+ *                 *workspace_bytes and returns PA_OK.  The contents need no
+ *                 initialization and are not meaningful after the call.
+ *   Supported: dtype PA_F32 or PA_BF16; head_dim 16, 32, 64, 128 or 256;
+ *   q_heads / kv_heads <= 16; any page_size >= 1.
+ */
+int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+              int32_t num_seqs, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+              int32_t num_pages, int32_t page_size, int32_t window, int32_t max_context_len,
+              float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

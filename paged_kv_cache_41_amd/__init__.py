@@ -1,0 +1,12 @@
+"""Paged K/V cache decode for AMD Instinct MI355X (gfx950).
+
+* ``ops`` -- torch binding of the C ABI (include/pa.h): ``store_kv``,
+  ``copy_pages``, ``decode``.  The HIP library is loaded on first call and a
+  missing library is an error, never a fallback.
+* ``alloc`` -- the host block allocator that produces block tables, slot
+  tables, new-row slots and copy-on-write copy lists.
+"""
+from . import alloc, ops
+from .alloc import OutOfPages, PagedKVCache
+
+__all__ = ["alloc", "ops", "OutOfPages", "PagedKVCache"]

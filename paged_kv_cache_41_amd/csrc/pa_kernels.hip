@@ -1,0 +1,445 @@
+// Paged K/V cache kernels for gfx950 (AMD Instinct MI355X, CDNA4) behind the C ABI of pa.h.
+//
+// Three operations of a decode step over a paged cache:
+//   * store_kv   -- scatter of the step's new K/V rows to their slots (mini-sglang
+//                   part 4, the KV buffer and its store: the pool is a list of token
+//                   rows and a slot list picks the row each new token goes to);
+//   * copy_pages -- whole-page copies behind copy-on-write (silicon-compiler chapter 15,
+//                   section "The model": a shared page is copied before it is written);
+//   * decode     -- single-query attention over the rows a block table reaches, limited
+//                   to the last W rows when a window is given (same chapter, sections
+//                   "The problem" and "The model"), split over chunks of rows with an
+//                   online (running max / running sum) softmax, then merged.
+//
+// Layout (all row-major): pool [num_pages, page_size, kv_heads, head_dim]; a token row is
+// kv_heads * head_dim contiguous elements, a (token, kv head) row head_dim contiguous
+// elements.  Logical row i of sequence s lives at page bt[s][i / page_size], offset
+// i % page_size.  Element offsets are computed in 64 bits.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_common.hpp"
+#include "pa_decode_mfma.hpp"
+
+namespace pa {
+
+// ------------------------------------------------------------------------------------
+// store_kv: one block per new token (grid-stride over tokens).  Rows move in units of U
+// (16 bytes when every pointer and the row size allow it, else 4 bytes).
+// ------------------------------------------------------------------------------------
+template <typename U>
+__global__ __launch_bounds__(256) void store_kv_kernel(
+    U* __restrict__ kp, U* __restrict__ vp, const U* __restrict__ kn, const U* __restrict__ vn,
+    const int32_t* __restrict__ slots, int num_tokens, int64_t num_slots, int units_per_row) {
+  for (int t = blockIdx.x; t < num_tokens; t += gridDim.x) {
+    const int slot = slots[t];
+    if (slot < 0 || (int64_t)slot >= num_slots) continue;
+    const U* ks = kn + (size_t)t * units_per_row;
+    const U* vs = vn + (size_t)t * units_per_row;
+    U* kd = kp + (size_t)slot * units_per_row;
+    U* vd = vp + (size_t)slot * units_per_row;
+    for (int i = threadIdx.x; i < units_per_row; i += blockDim.x) {
+      kd[i] = ks[i];
+      vd[i] = vs[i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// copy_pages: blockIdx.y walks the copy list, blockIdx.z picks K (0) or V (1), x and the
+// threads stride over the page in units of U.
+// ------------------------------------------------------------------------------------
+template <typename U>
+__global__ __launch_bounds__(256) void copy_pages_kernel(
+    U* __restrict__ kp, U* __restrict__ vp, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ dst, int num_copies, int num_pages, int64_t units_per_page) {
+  U* pool = blockIdx.z ? vp : kp;
+  for (int c = blockIdx.y; c < num_copies; c += gridDim.y) {
+    const int s = src[c], d = dst[c];
+    if (s < 0 || s >= num_pages || d < 0 || d >= num_pages) continue;
+    const U* from = pool + (size_t)s * units_per_page;
+    U* to = pool + (size_t)d * units_per_page;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < units_per_page;
+         i += (int64_t)gridDim.x * blockDim.x)
+      to[i] = from[i];
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// decode, generic VALU path (any dtype, head_dim 16..256, group <= 16, any page size).
+//
+// One wavefront per (sequence, kv head, chunk).  A (token, kv head) row of head_dim
+// elements is spread over LPT lanes holding 16 bytes each, so one wave covers TPW
+// tokens per iteration with fully used 16-byte loads.  Logits are reduced across the
+// LPT lanes with xor shuffles, leaving every lane of a token with the logits of all
+// query heads of the group; the running max is shared by the whole wave, the running
+// sum and the output accumulator are kept per token group and summed at the end.
+// Logits are in base 2: q is pre-multiplied by scale * log2(e) and exp2 is used.
+// ------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&x)[16 / sizeof(T)]);
+
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename T, int D, int GMAX>
+__global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = 64 / LPT;
+  static_assert(D % EPL == 0 && LPT <= 64 && (LPT & (LPT - 1)) == 0, "unsupported head_dim");
+
+  const int lane = threadIdx.x;
+  const int Hkv = a.kv_heads;
+  const int g = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int c = rest % a.max_chunks;
+  const int s = rest / a.max_chunks;
+  const int G = a.group;
+  const int sub = lane % LPT;
+  const int tok = lane / LPT;
+
+  int L, lo, n;
+  live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
+  const int nch = (n + a.chunk - 1) / a.chunk;
+  float* outp = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * D + sub * EPL;
+  if (nch == 0) {
+    if (c == 0 && tok == 0)
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) outp[(size_t)h * D + e] = 0.f;
+    return;
+  }
+  if (c >= nch) return;
+
+  const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)s * a.q_heads + (size_t)g * G) * D + sub * EPL;
+  float qv[GMAX][EPL];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+      load16<T>(qb + (size_t)h * D, qv[h]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[h][e] = 0.f;
+    }
+  }
+  float m[GMAX], l[GMAX], acc[GMAX][EPL];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const T* kp = reinterpret_cast<const T*>(a.k_pool);
+  const T* vp = reinterpret_cast<const T*>(a.v_pool);
+  const size_t row_stride = (size_t)Hkv * D;
+  const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
+  const int t_begin = lo + c * a.chunk;
+  const int t_end = min(L, t_begin + a.chunk);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += TPW) {
+    const int t = t0 + tok;
+    bool valid = t < t_end;
+    float kx[EPL], vx[EPL];
+    if (valid) {
+      const int page = btr[t / a.page_size];
+      valid = page >= 0 && page < a.num_pages;
+      if (valid) {
+        const size_t off = ((size_t)page * a.page_size + t % a.page_size) * row_stride +
+                           (size_t)g * D + sub * EPL;
+        load16<T>(kp + off, kx);
+        load16<T>(vp + off, vx);
+      }
+    }
+    if (!valid) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kx[e] = vx[e] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h >= G) continue;
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sc = fmaf(qv[h][e], kx[e], sc);
+#pragma unroll
+      for (int o = LPT / 2; o >= 1; o >>= 1) sc += __shfl_xor(sc, o, 64);
+      if (!valid) sc = -INFINITY;
+      float mt = sc;
+#pragma unroll
+      for (int o = LPT; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+      const float mnew = fmaxf(m[h], mt);
+      if (mnew == -INFINITY) continue;
+      const float alpha = exp2f(m[h] - mnew);
+      const float p = valid ? exp2f(sc - mnew) : 0.f;
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e] * alpha);
+      m[h] = mnew;
+    }
+  }
+
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h >= G) continue;
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1) {
+      l[h] += __shfl_xor(l[h], o, 64);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+    }
+  }
+  if (tok != 0) return;
+  if (nch == 1) {
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / l[h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) outp[(size_t)h * D + e] = acc[h][e] * inv;
+    }
+  } else {
+    for (int h = 0; h < G; ++h) {
+      const size_t part = ((size_t)s * a.q_heads + (size_t)g * G + h) * a.max_chunks + c;
+      if (sub == 0) {
+        a.ws_ml[2 * part] = m[h];
+        a.ws_ml[2 * part + 1] = l[h];
+      }
+      float* wa = a.ws_acc + part * D + sub * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) wa[e] = acc[h][e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// merge: one block per (sequence, query head) whose rows were split over several chunks.
+// out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, chunks in fixed order.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int D) {
+  const int h = blockIdx.x % a.q_heads;
+  const int s = blockIdx.x / a.q_heads;
+  int L, lo, n;
+  live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
+  const int nch = (n + a.chunk - 1) / a.chunk;
+  if (nch <= 1) return;
+  const size_t base = ((size_t)s * a.q_heads + h) * a.max_chunks;
+  const float* ml = a.ws_ml + 2 * base;
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
+  float den = 0.f;
+  for (int c = 0; c < nch; ++c) den += exp2f(ml[2 * c] - M) * ml[2 * c + 1];
+  const float inv = 1.f / den;
+  const float* acc = a.ws_acc + base * D;
+  float* out = a.out + ((size_t)s * a.q_heads + h) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float num = 0.f;
+    for (int c = 0; c < nch; ++c) num += exp2f(ml[2 * c] - M) * acc[(size_t)c * D + d];
+    out[d] = num * inv;
+  }
+}
+
+using DecodeFn = void (*)(DecodeArgs);
+
+template <typename T, int D>
+DecodeFn pick_generic(int group) {
+  if (group <= 1) return decode_generic_kernel<T, D, 1>;
+  if (group <= 2) return decode_generic_kernel<T, D, 2>;
+  if (group <= 4) return decode_generic_kernel<T, D, 4>;
+  if (group <= 8) return decode_generic_kernel<T, D, 8>;
+  return decode_generic_kernel<T, D, 16>;
+}
+
+template <typename T>
+DecodeFn pick_generic_d(int head_dim, int group) {
+  switch (head_dim) {
+    case 16: return pick_generic<T, 16>(group);
+    case 32: return pick_generic<T, 32>(group);
+    case 64: return pick_generic<T, 64>(group);
+    case 128: return pick_generic<T, 128>(group);
+    case 256: return pick_generic<T, 256>(group);
+    default: return nullptr;
+  }
+}
+
+inline int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rows per chunk: a power of two between 16 and 512, about one eighth of the longest
+// attended range, so long contexts split into enough chunks to fill the chip and
+// short ones stay in one chunk (no merge).
+inline int pick_chunk(int max_live) {
+  int want = (max_live + 7) / 8;
+  int c = 16;
+  while (c < want && c < 512) c <<= 1;
+  return c;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported combination";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int pa_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_pages,
+                           int32_t page_size, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                           void* stream) {
+  if (num_tokens < 0 || num_pages <= 0 || page_size <= 0 || kv_heads <= 0 || head_dim <= 0)
+    return PA_EINVAL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_EINVAL;
+  const int64_t row_bytes = (int64_t)kv_heads * head_dim * elt_bytes(dtype);
+  if (row_bytes % 4) return PA_EUNSUPPORTED;
+  const int64_t num_slots = (int64_t)num_pages * page_size;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int grid = num_tokens < 65535 ? num_tokens : 65535;
+  if (row_bytes % 16 == 0 && aligned16(k_pool) && aligned16(v_pool) && aligned16(k_new) &&
+      aligned16(v_new)) {
+    hipLaunchKernelGGL(store_kv_kernel<uint4>, dim3(grid), dim3(128), 0, st,
+                       (uint4*)k_pool, (uint4*)v_pool, (const uint4*)k_new, (const uint4*)v_new,
+                       slot_mapping, num_tokens, num_slots, (int)(row_bytes / 16));
+  } else {
+    hipLaunchKernelGGL(store_kv_kernel<uint32_t>, dim3(grid), dim3(128), 0, st,
+                       (uint32_t*)k_pool, (uint32_t*)v_pool, (const uint32_t*)k_new,
+                       (const uint32_t*)v_new, slot_mapping, num_tokens, num_slots,
+                       (int)(row_bytes / 4));
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_pages,
+                             const int32_t* dst_pages, int32_t num_copies, int32_t num_pages,
+                             int32_t page_size, int32_t kv_heads, int32_t head_dim,
+                             int32_t dtype, void* stream) {
+  if (num_copies < 0 || num_pages <= 0 || page_size <= 0 || kv_heads <= 0 || head_dim <= 0)
+    return PA_EINVAL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  if (num_copies == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_pages || !dst_pages) return PA_EINVAL;
+  const int64_t page_bytes = (int64_t)page_size * kv_heads * head_dim * elt_bytes(dtype);
+  if (page_bytes % 4) return PA_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int gy = num_copies < 65535 ? num_copies : 65535;
+  if (page_bytes % 16 == 0 && aligned16(k_pool) && aligned16(v_pool)) {
+    const int64_t units = page_bytes / 16;
+    const int gx = (int)((units + 256 * 4 - 1) / (256 * 4));
+    hipLaunchKernelGGL(copy_pages_kernel<uint4>, dim3(gx, gy, 2), dim3(256), 0, st,
+                       (uint4*)k_pool, (uint4*)v_pool, src_pages, dst_pages, num_copies,
+                       num_pages, units);
+  } else {
+    const int64_t units = page_bytes / 4;
+    const int gx = (int)((units + 256 * 4 - 1) / (256 * 4));
+    hipLaunchKernelGGL(copy_pages_kernel<uint32_t>, dim3(gx, gy, 2), dim3(256), 0, st,
+                       (uint32_t*)k_pool, (uint32_t*)v_pool, src_pages, dst_pages, num_copies,
+                       num_pages, units);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t bt_stride,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                         int32_t kv_heads, int32_t head_dim, int32_t num_pages,
+                         int32_t page_size, int32_t window, int32_t max_context_len, float scale,
+                         int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return PA_EINVAL;
+  if (num_seqs < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || num_pages <= 0 ||
+      page_size <= 0 || bt_stride <= 0)
+    return PA_EINVAL;
+  if (q_heads % kv_heads) return PA_EINVAL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  if (!(scale == scale)) return PA_EINVAL;
+  const int group = q_heads / kv_heads;
+  const int64_t table_rows = (int64_t)bt_stride * page_size;
+  if (max_context_len <= 0) max_context_len = table_rows > INT32_MAX ? INT32_MAX : (int32_t)table_rows;
+  if ((int64_t)max_context_len > table_rows) return PA_EINVAL;
+  if (group > 16) return PA_EUNSUPPORTED;
+
+  DecodeFn generic = dtype == PA_F32 ? pick_generic_d<float>(head_dim, group)
+                                     : pick_generic_d<uint16_t>(head_dim, group);
+  if (!generic) return PA_EUNSUPPORTED;
+
+  const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
+  DecodeArgs a{};
+  a.chunk = pick_chunk(max_live);
+  const bool fast = mfma::eligible(dtype, head_dim, group);
+  if (fast) a.chunk = mfma::chunk_for(max_live);
+  a.max_chunks = (max_live + a.chunk - 1) / a.chunk;
+  if (a.max_chunks < 1) a.max_chunks = 1;
+  const size_t parts = (size_t)num_seqs * q_heads * a.max_chunks;
+  const size_t need = parts * ((size_t)head_dim + 2) * sizeof(float);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return PA_OK;
+  }
+  if (*workspace_bytes < need) return PA_EWORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_EUNSUPPORTED;
+
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.window = window > 0 ? window : 0;
+  a.max_ctx = max_context_len;
+  a.qscale = scale * 1.4426950408889634f;
+  a.ws_ml = reinterpret_cast<float*>(workspace);
+  a.ws_acc = a.ws_ml + 2 * parts;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t blocks = (int64_t)num_seqs * a.max_chunks * kv_heads;
+  if (blocks * 256 > INT32_MAX) return PA_EUNSUPPORTED;
+  if (fast) {
+    if (mfma::launch(a, st) != 0) return PA_ELAUNCH;
+  } else {
+    hipLaunchKernelGGL(generic, dim3((unsigned)blocks), dim3(64), 0, st, a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  if (a.max_chunks > 1) {
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * q_heads)), dim3(128), 0, st, a,
+                       (int)head_dim);
+    if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  }
+  return PA_OK;
+}

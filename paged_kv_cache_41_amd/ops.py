@@ -1,0 +1,137 @@
+"""Torch-facing binding of the three C-ABI entry points.
+
+Argument marshalling only: shape, dtype, device and contiguity checks, then
+raw device pointers and the current HIP stream go to libpa.so.  Every step of
+the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    d = ts[0].device
+    if d.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    for t in ts:
+        if t.device != d:
+            raise ValueError("tensors are on different devices")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return d
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
+def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.dtype != v_pool.dtype:
+        raise ValueError("pools must both be [num_pages, page_size, kv_heads, head_dim]")
+    return tuple(int(x) for x in k_pool.shape)
+
+
+def store_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
+    """Write row t of k_new/v_new to flat slot slot_mapping[t] of the pools (in place)."""
+    dev = _dev(k_pool, v_pool, k_new, v_new, slot_mapping)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    T = int(slot_mapping.numel())
+    if k_new.shape != (T, hkv, d) or v_new.shape != (T, hkv, d):
+        raise ValueError("new rows must be [num_tokens, kv_heads, head_dim]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("new rows must have the pool dtype")
+    _i32(slot_mapping, "slot_mapping")
+    lib = _lib.load()
+    _lib.check("pa_store_kv", lib.pa_store_kv(
+        k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        slot_mapping.data_ptr(), T, n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
+
+
+def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
+    """pool[dst[i]] = pool[src[i]] for K and V, whole pages (in place)."""
+    dev = _dev(k_pool, v_pool, src_pages, dst_pages)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    if src_pages.numel() != dst_pages.numel():
+        raise ValueError("source and target lists differ in length")
+    _i32(src_pages, "src_pages")
+    _i32(dst_pages, "dst_pages")
+    lib = _lib.load()
+    _lib.check("pa_copy_pages", lib.pa_copy_pages(
+        k_pool.data_ptr(), v_pool.data_ptr(), src_pages.data_ptr(), dst_pages.data_ptr(),
+        int(src_pages.numel()), n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
+
+
+def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, scale,
+                 max_context_len, ws_ptr, ws_size, stream_handle):
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    B, hq, dq = (int(x) for x in q.shape)
+    lib = _lib.load()
+    size = ctypes.c_size_t(ws_size)
+    st = lib.pa_decode(
+        out.data_ptr() if out is not None else None, q.data_ptr(), k_pool.data_ptr(),
+        v_pool.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
+        context_lens.data_ptr(), B, hq, hkv, d, n, P, int(window), int(max_context_len),
+        float(scale), _code(q), ws_ptr, ctypes.byref(size), stream_handle)
+    _lib.check("pa_decode", st)
+    return size.value
+
+
+def decode_workspace_bytes(q, k_pool, v_pool, block_tables, context_lens, *, window=0,
+                           max_context_len=0) -> int:
+    """Bytes of device workspace ``decode`` needs for these operands."""
+    return _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, 1.0,
+                        max_context_len, None, 0, None)
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
+           scale: Optional[float] = None, max_context_len: int = 0,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Single-query paged attention; returns fp32 ``[num_seqs, q_heads, head_dim]``.
+
+    A raw token-slot table is passed as ``block_tables`` together with pools
+    viewed in pages of one row (``pool.view(-1, 1, kv_heads, head_dim)``).
+    """
+    dev = _dev(q, k_pool, v_pool, block_tables, context_lens)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_seqs, q_heads, head_dim] in the pool dtype")
+    B = int(q.shape[0])
+    if block_tables.dim() != 2 or block_tables.shape[0] < B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [>= num_seqs, stride], context_lens [num_seqs]")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(B, q.shape[1], d, dtype=torch.float32, device=dev)
+    elif out.shape != (B, q.shape[1], d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [num_seqs, q_heads, head_dim]")
+    need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, scale,
+                        max_context_len, None, 0, None)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, scale,
+                 max_context_len, workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    return out
