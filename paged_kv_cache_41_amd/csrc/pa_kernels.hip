@@ -393,8 +393,8 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
   DecodeArgs a{};
   a.chunk = pick_chunk(max_live);
-  const bool fast = mfma::eligible(dtype, head_dim, group);
-  if (fast) a.chunk = mfma::chunk_for(max_live);
+  const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
+  if (fast) a.chunk = mfma::chunk_for(num_seqs, kv_heads, max_live);
   a.max_chunks = (max_live + a.chunk - 1) / a.chunk;
   if (a.max_chunks < 1) a.max_chunks = 1;
   const size_t parts = (size_t)num_seqs * q_heads * a.max_chunks;

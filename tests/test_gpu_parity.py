@@ -109,6 +109,11 @@ EDGE = {
     "long_multichunk": dict(num_seqs=3, q_heads=8, kv_heads=2, head_dim=128, len_lo=3000, len_hi=9000),
     "long_window": dict(num_seqs=3, q_heads=8, kv_heads=2, head_dim=128, window=2000, len_lo=2500, len_hi=9000),
     "empty_and_one": dict(num_seqs=4, q_heads=8, kv_heads=2, head_dim=128, lens=(0, 1, 0, 2)),
+    "page3_generic": dict(q_heads=8, kv_heads=2, head_dim=128, page_size=3, len_lo=1, len_hi=400),
+    "page32": dict(q_heads=12, kv_heads=4, head_dim=128, page_size=32, len_lo=1, len_hi=900),
+    "page64_window": dict(q_heads=8, kv_heads=8, head_dim=128, page_size=64, window=100, len_lo=1, len_hi=900),
+    "group3": dict(q_heads=6, kv_heads=2, head_dim=128, len_lo=1, len_hi=500),
+    "group12_long": dict(num_seqs=3, q_heads=24, kv_heads=2, head_dim=128, len_lo=1500, len_hi=6000),
 }
 
 
