@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", type=str, default=None,
                    help="JSON file with measured HBM bytes per decode launch")
+    p.add_argument("--no-copy-ceiling", action="store_true",
+                   help="skip the device-to-device copy reference measurement")
     return p.parse_args()
 
 
@@ -72,6 +74,27 @@ def unique_kv_bytes(sc) -> int:
     rows_per = P if P > 1 else 1
     # rows of each distinct page that some sequence attends (approximate at page grain)
     return len(seen) * rows_per * 2 * s.kv_heads * s.head_dim * elt
+
+
+def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
+    """Bandwidth of a plain device-to-device copy (torch's copy kernel) of known size:
+    a measured reference next to the nominal peak, and the calibration kernel for the
+    HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / reps * 1e-3
+    return {"bytes_read": nbytes, "bytes_written": nbytes,
+            "gbps_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}
 
 
 def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
@@ -221,6 +244,8 @@ def main():
     }
     if s.prefix_len:
         result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
+    if not args.no_copy_ceiling:
+        result["hbm_copy_reference"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc)
     print(json.dumps(result), flush=True)

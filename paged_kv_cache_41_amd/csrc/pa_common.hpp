@@ -19,8 +19,12 @@ struct DecodeArgs {
   int max_ctx;                 // host bound on context lengths; longer ones are clamped to it
   int max_chunks, chunk;       // rows per chunk; chunks per sequence at most
   float qscale;                // scale * log2(e): logits are kept in base 2
-  float* ws_ml;                // [num_seqs, q_heads, max_chunks, 2]: running max, running sum
-  float* ws_acc;               // [num_seqs, q_heads, max_chunks, head_dim]
+  float* ws_ml;                // partial running max and running sum, pairs
+  float* ws_acc;               // partial accumulators, head_dim floats each
+  int* ws_cum;                 // streaming path: per-sequence tile prefix sums
+  int* ws_wave_start;          // streaming path: first tile of each wavefront's range
+  int* ws_rec;                 // streaming path: per-wavefront merge records (4 ints)
+  int total_waves;             // streaming path: wavefronts sharing the tile list
 };
 
 // Rows attended by a sequence with `ctx` rows: [lo, L) with L = ctx clamped to

@@ -70,6 +70,12 @@ struct Tile {
   uint64_t valid;    // bit t: token t0 + t is attended and mapped
 };
 
+// Rescale threshold in base-2 logit units: the running reference max is only raised
+// when a tile's max exceeds it by more than this, so probabilities stay below 2^8
+// and most tiles skip the rescale entirely.  The result is the same softmax: every
+// probability and the running sum use one reference until it changes.
+constexpr float RESCALE_T = 8.f;
+
 template <int GMAX>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int s_pages[MAX_CHUNK + 2];
@@ -111,57 +117,60 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pool);
-  const size_t rs = (size_t)Hkv * HD;  // elements per token row
-  const size_t head_off = (size_t)g * HD;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
+  const uint32_t page_bytes = row_bytes * (uint32_t)P;
   const int col = lane & 15;           // K token / score head / V 16-byte column block
   const int grp = lane >> 4;           // K head_dim slice / score token group / V token
+  const uint32_t k_lane = (uint32_t)g * HD * 2 + grp * 64;
+  const uint32_t v_lane = (uint32_t)g * HD * 2 + col * 16;
+  const int last_page = a.num_pages - 1;
 
   // query vectors of the group as the B operand: head col, head_dim slice grp
   bf16x8 qb[4];
   {
     const uint4 zero = make_uint4(0, 0, 0, 0);
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((size_t)s * a.q_heads + (size_t)g * G + col) * HD + grp * 32;
+                           ((size_t)s * a.q_heads + (size_t)g * G + (col < G ? col : 0)) * HD +
+                           grp * 32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qb[j] = as_bf16x8(col < G ? *reinterpret_cast<const uint4*>(qrow + 8 * j) : zero);
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * j);
+      qb[j] = as_bf16x8(col < G ? v : zero);
+    }
   }
 
   const int ntile = (t_end - t_begin + TILE - 1) / TILE;
 
+  auto row_addr = [&](const char* base, int pg, int t, uint32_t lane_off) {
+    // pg is clamped into [0, num_pages) by the callers; a page is < 4 GiB
+    return reinterpret_cast<const uint4*>(base + (uint64_t)(uint32_t)pg * page_bytes +
+                                          ((uint32_t)(t & (P - 1)) * row_bytes + lane_off));
+  };
+
+  // Loads are branch-free so that the compiler can keep several tiles in flight: a row
+  // past the end of the chunk, or one whose table entry is unmapped (a caller error
+  // inside the attended range), is still read from a clamped in-pool address, and the
+  // validity mask keeps it out of the softmax (scores) and out of P.V (values are
+  // replaced, not multiplied, so poison in unread pages cannot leak).
   auto load_tile = [&](int tile, Tile& T) {
     const int t0 = t_begin + tile * TILE;
-    const int tk = t0 + col;
-    bool ok = tk < t_end;
-    int pg = ok ? s_pages[(tk >> lp) - j0] : -1;
-    ok = ok && pg >= 0;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    if (ok) {
-      const uint16_t* src = kp + ((size_t)pg * P + (tk & (P - 1))) * rs + head_off + grp * 32;
+    const int tk = min(t0 + col, t_end - 1);
+    const int ek = s_pages[(tk >> lp) - j0];
+    T.valid = __ballot(t0 + col < t_end && ek >= 0);
+    const uint4* kp = row_addr(kbase, min(max(ek, 0), last_page), tk, k_lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) T.k[j] = *reinterpret_cast<const uint4*>(src + 8 * j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) T.k[j] = zero;
-    }
-    T.valid = __ballot(ok);
+    for (int j = 0; j < 4; ++j) T.k[j] = kp[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tt = grp + 4 * i;
-      const int tv = t0 + tt;
-      if ((T.valid >> tt) & 1) {
-        const int pv = s_pages[(tv >> lp) - j0];
-        T.v[i] = *reinterpret_cast<const uint4*>(
-            vp + ((size_t)pv * P + (tv & (P - 1))) * rs + head_off + col * 8);
-      } else {
-        T.v[i] = zero;
-      }
+      const int tv = min(t0 + grp + 4 * i, t_end - 1);
+      const int ev = s_pages[(tv >> lp) - j0];
+      T.v[i] = *row_addr(vbase, min(max(ev, 0), last_page), tv, v_lane);
     }
   };
 
-  float m_run = -INFINITY;  // per score column (head col)
+  float m_ref = -INFINITY;  // reference max of score column col (its query head)
   float l_run = 0.f;
   float acc[GMAX][8];
 #pragma unroll
@@ -170,55 +179,61 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   float(*pt)[PROW] = s_p[w];
-  Tile cur;
-  if (w < ntile) load_tile(w, cur);
-  for (int tile = w; tile < ntile; tile += NW) {
-    Tile nxt;
-    const bool more = tile + NW < ntile;
-    if (more) load_tile(tile + NW, nxt);
 
+  auto compute = [&](const Tile& T) {
     // scores: S[token][head] = K . q
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[j]), qb[j], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[j]), qb[j], sc, 0, 0, 0);
     float sv[4];
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = (cur.valid >> (4 * grp + r)) & 1;
+      const bool ok = (T.valid >> (4 * grp + r)) & 1;
       sv[r] = ok ? sc[r] * a.qscale : -INFINITY;
       mt = fmaxf(mt, sv[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m_run, mt);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    const float alpha = exp2f(m_run - ms);
+    // raise the reference when some head's tile max passes it by more than RESCALE_T
+    const bool raise = __ballot(col < G && mt > m_ref + RESCALE_T) != 0;
+    if (raise) {
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);  // 0 when m_ref = -inf
+      l_run *= alpha;
+      m_ref = mn;
+      if (grp == 0 && col < G) pt[TILE][col] = alpha;
+    }
+    const float ms = m_ref == -INFINITY ? 0.f : m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = exp2f(sv[r] - ms);
+      const float p = __builtin_amdgcn_exp2f(sv[r] - ms);
       psum += p;
       if (col < G) pt[4 * grp + r][col] = p;
     }
-    if (grp == 0 && col < G) pt[TILE][col] = alpha;
-    l_run = l_run * alpha + psum;
-    m_run = mn;
+    l_run += psum;
     wave_lds_sync();
 
     // P.V on the vector ALUs
-    float al[GMAX];
+    if (raise) {
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h) al[h] = pt[TILE][h];
+      for (int h = 0; h < GMAX; ++h) {
+        const float al = pt[TILE][h];
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+      }
+    }
+    const bool full = T.valid == ~0ull;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float vx[8];
-      bf16x8_to_f32(cur.v[i], vx);
+      bf16x8_to_f32(T.v[i], vx);
+      if (!full && !((T.valid >> (grp + 4 * i)) & 1)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vx[e] = 0.f;
+      }
       const float* prow = pt[grp + 4 * i];
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
@@ -228,7 +243,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     wave_lds_sync();
-    if (more) cur = nxt;
+  };
+
+  // Three register stages: compute one tile while the next two are in flight.  Loads
+  // are issued unconditionally; past this wave's last tile they re-read that tile (a
+  // cache hit), so no branch separates a load from its use and the compiler can keep
+  // the stages in fixed registers.  Only the compute steps are guarded.
+  const int ntw = ntile > w ? (ntile - w + NW - 1) / NW : 0;  // tiles of this wave
+  if (ntw > 0) {
+    auto tile_of = [&](int i) { return w + NW * min(i, ntw - 1); };
+    Tile A, B, C;
+    load_tile(tile_of(0), A);
+    load_tile(tile_of(1), B);
+    for (int i = 0; i < ntw; i += 3) {
+      load_tile(tile_of(i + 2), C);
+      compute(A);
+      load_tile(tile_of(i + 3), A);
+      if (i + 1 < ntw) compute(B);
+      load_tile(tile_of(i + 4), B);
+      if (i + 2 < ntw) compute(C);
+    }
   }
 
   // per-wave totals: running sum over the score token groups, accumulator over V token groups
@@ -242,7 +276,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
     }
   if (lane < 16) {
-    s_m[w][lane] = m_run;
+    s_m[w][lane] = m_ref;
     s_l[w][lane] = l_run;
 #pragma unroll
     for (int h = 0; h < GMAX; ++h)

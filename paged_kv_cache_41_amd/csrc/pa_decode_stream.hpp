@@ -1,0 +1,476 @@
+// Balanced streaming decode: bf16 pools, head_dim 128, up to 16 query heads per kv head,
+// page sizes that are powers of two, up to STREAM_BMAX sequences.
+//
+// Work is the flattened list of 16-row tiles of every (sequence, kv head) segment:
+// segment (s, g) covers the tiles of rows [lo_s, L_s) aligned to 16-row boundaries,
+// segments are ordered by s then g.  A resident grid of W wavefronts splits that list
+// into W contiguous ranges of equal length, so every wavefront streams the same number
+// of tiles with no per-item start-up, no empty work items and no ragged tail.  A range
+// can cross segment boundaries; the pipeline crosses them too.
+//
+// Every workgroup first turns the context lengths into per-sequence tile counts and an
+// exclusive prefix sum in LDS (workgroup 0 also stores it for the merge kernel).  Each
+// wavefront then runs a three-stage software pipeline over its tiles: the block-table
+// entry of tile i+3 (one per lane, for token t0 + lane % 16), the K and V rows of tile
+// i+2, and the compute of tile i.  All loads are unconditional: a row outside the
+// attended range or behind an unmapped entry is read from a clamped address inside the
+// pool and masked out of the softmax and P.V; past the end of the range the last tile
+// is re-read (a cache hit).
+//
+// Compute per tile is the matrix-core score tile (K as the A operand of four
+// v_mfma_f32_16x16x32_bf16, the group's queries as the B operand), base-2 online
+// softmax with a lazily raised reference max, and P.V in fp32 on the vector ALUs from
+// 16-byte column blocks of V.  A segment that starts and ends inside one wavefront
+// writes its output directly; the first and last segment of a range may be cut and
+// are written as partial (max, sum, accumulator) to one of two slots of that
+// wavefront, which the merge kernel combines in a fixed order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_common.hpp"
+#include "pa_decode_mfma.hpp"
+
+namespace pa {
+namespace stream {
+
+using mfma::as_bf16x8;
+using mfma::bf16x8;
+using mfma::bf16x8_to_f32;
+using mfma::f32x4;
+using mfma::wave_lds_sync;
+
+constexpr int HD = 128;
+constexpr int TILE = 16;
+constexpr int NW = 4;           // wavefronts per workgroup
+constexpr int BMAX = 2048;      // sequences handled by this path
+constexpr int PROW = 20;
+constexpr int GSTRIDE = 16;     // heads per partial slot
+constexpr float RESCALE_T = 8.f;
+
+struct Tile {
+  uint4 k[4];
+  uint4 v[4];
+  uint64_t valid;
+};
+
+// Position of a tile in the flattened list, with the fields of its segment.
+struct Cur {
+  int s, g, k;      // sequence, kv head, tile within the segment
+  int tiles;        // tiles of the segment
+  int lo, L;        // attended rows [lo, L)
+  int t0base;       // first row of tile 0: lo rounded down to a multiple of 16
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int GMAX>
+__global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
+  __shared__ int s_cum[BMAX + 1];   // tiles of sequences before s
+  __shared__ int s_len[BMAX];       // clamped context length
+  __shared__ int s_scan[64 * NW];
+  __shared__ float s_p[NW][TILE + 1][PROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int B = a.num_seqs;
+  const int Hkv = a.kv_heads;
+  const int G = a.group;
+
+  // ---- per-sequence tile counts and their exclusive prefix sum --------------------------
+  {
+    const int per = (B + 64 * NW - 1) / (64 * NW);
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = tid * per + i;
+      if (s < B) {
+        int L, lo, n;
+        live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
+        const int t = n > 0 ? ((L - 1) >> 4) - (lo >> 4) + 1 : 0;
+        s_len[s] = L;
+        s_cum[s] = t;
+        local += t;
+      }
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 64 * NW; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int run = tid > 0 ? s_scan[tid - 1] : 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = tid * per + i;
+      if (s < B) {
+        const int t = s_cum[s];
+        s_cum[s] = run;
+        run += t;
+      }
+    }
+    if (tid == 0) s_cum[B] = s_scan[64 * NW - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += 64 * NW) a.ws_cum[i] = s_cum[i];
+  }
+
+  // ---- this wavefront's range of tiles ----------------------------------------------------
+  const int64_t T = (int64_t)Hkv * s_cum[B];
+  const int W = a.total_waves;
+  const int kw = blockIdx.x * NW + w;
+  const int ta = (int)((int64_t)kw * T / W);
+  const int n = (int)((int64_t)(kw + 1) * T / W) - ta;
+  if (lane == 0) {
+    a.ws_wave_start[kw] = ta;
+    reinterpret_cast<int4*>(a.ws_rec)[kw] = make_int4(-1, 0, 0, 0);
+  }
+  if (n <= 0) return;
+
+  const int P = a.page_size;
+  const int lp = 31 - __clz(P);
+  const int last_page = a.num_pages - 1;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
+  const uint32_t page_bytes = row_bytes * (uint32_t)P;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  auto seg_fields = [&](Cur& c) {
+    c.tiles = uni(s_cum[c.s + 1] - s_cum[c.s]);
+    c.L = uni(s_len[c.s]);
+    c.lo = (a.window > 0 && c.L > a.window) ? c.L - a.window : 0;
+    c.t0base = (c.lo >> 4) << 4;
+  };
+  // one past the flattened index of the segment's last tile
+  auto seg_end_flat = [&](const Cur& c) {
+    return Hkv * s_cum[c.s] + (c.g + 1) * c.tiles;
+  };
+  // locate flattened tile ta
+  Cur cc;
+  {
+    int lo_s = 0, hi_s = B - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if ((int64_t)Hkv * s_cum[mid] <= ta) lo_s = mid; else hi_s = mid - 1;
+    }
+    cc.s = uni(lo_s);
+    seg_fields(cc);
+    const int within = ta - Hkv * s_cum[cc.s];
+    cc.g = uni(within / cc.tiles);
+    cc.k = uni(within % cc.tiles);
+  }
+  // advance to the next tile; `more` is false at the last tile of the range (the cursor
+  // then stays, so the stages re-read it)
+  auto advance = [&](Cur& c, bool more) {
+    if (!more) return;
+    if (c.k + 1 < c.tiles) {
+      c.k += 1;
+      return;
+    }
+    c.k = 0;
+    c.g += 1;
+    if (c.g == Hkv) {
+      c.g = 0;
+      do { c.s += 1; } while (s_cum[c.s + 1] == s_cum[c.s]);
+      c.s = uni(c.s);
+      seg_fields(c);
+    }
+  };
+
+  auto table_entry = [&](const Cur& c) {
+    const int t = min(max(c.t0base + c.k * TILE + col, c.lo), c.L - 1);
+    return a.block_tables[(size_t)c.s * a.bt_stride + (t >> lp)];
+  };
+
+  auto row_addr = [&](const char* base, int pg, int t, uint32_t lane_off) {
+    return reinterpret_cast<const uint4*>(base + (uint64_t)(uint32_t)pg * page_bytes +
+                                          ((uint32_t)(t & (P - 1)) * row_bytes + lane_off));
+  };
+
+  // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + grp + 4 i (16 B at
+  // column block col); e = table entry of token t0 + col
+  auto load_tile = [&](const Cur& c, int e, Tile& Tl) {
+    const int t0 = c.t0base + c.k * TILE;
+    const int tk = t0 + col;
+    Tl.valid = __ballot(tk >= c.lo && tk < c.L && e >= 0 && e <= last_page);
+    const uint32_t hoff = (uint32_t)c.g * HD * 2;
+    const int tkc = min(max(tk, c.lo), c.L - 1);
+    const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ev = __shfl(e, grp + 4 * i, 64);
+      const int tv = min(max(t0 + grp + 4 * i, c.lo), c.L - 1);
+      Tl.v[i] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
+    }
+  };
+
+  // ---- per-segment state -----------------------------------------------------------------
+  bf16x8 qb[4];
+  float m_ref = -INFINITY, l_run = 0.f;
+  float acc[GMAX][8];
+  bool first_seg = true;     // the segment being computed is the first of this range
+  bool started_here = false; // ... and this wavefront computed its tile 0
+  float(*pt)[PROW] = s_p[w];
+
+  auto begin_segment = [&](const Cur& c) {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((size_t)c.s * a.q_heads + (size_t)c.g * G + (col < G ? col : 0)) * HD +
+                           grp * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * j);
+      qb[j] = as_bf16x8(col < G ? v : zero);
+    }
+    // Wait here, on this rare path, for the query rows: otherwise the compiler would
+    // have to assume the load may still be outstanding wherever the query registers
+    // are read and drain every prefetched tile before each tile's compute.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    m_ref = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    started_here = c.k == 0;
+  };
+
+  auto end_segment = [&](const Cur& c, bool complete) {
+    float lt = l_run;
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[h][e] += __shfl_xor(acc[h][e], 16, 64);
+        acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
+      }
+    if (complete) {
+      float* out = a.out + ((size_t)c.s * a.q_heads + (size_t)c.g * G) * HD + col * 8;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const float lh = __shfl(lt, h, 64);
+        if (h < G && lane < 16) {
+          const float inv = lh > 0.f ? 1.f / lh : 0.f;
+          float4* o = reinterpret_cast<float4*>(out + (size_t)h * HD);
+          o[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+          o[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+        }
+      }
+    } else {
+      const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
+      if (started_here && lane == 0) {
+        // this wavefront holds the first piece of a segment cut at its range end: leave
+        // the merge kernel a record (segment, slot of this piece, flattened end)
+        int4* rec = reinterpret_cast<int4*>(a.ws_rec);
+        rec[kw] = make_int4(c.s * Hkv + c.g, first_seg ? 0 : 1, seg_end_flat(c), 0);
+      }
+      if (lane < G) {
+        a.ws_ml[(pi * GSTRIDE + lane) * 2] = m_ref;
+        a.ws_ml[(pi * GSTRIDE + lane) * 2 + 1] = lt;
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          if (h < G) {
+            float4* o = reinterpret_cast<float4*>(a.ws_acc + (pi * GSTRIDE + h) * HD + col * 8);
+            o[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            o[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+          }
+        }
+      }
+    }
+    first_seg = false;
+  };
+
+  auto compute = [&](const Tile& Tl, const Cur& c, int i) {
+    if (i == 0 || c.k == 0) begin_segment(c);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[j]), qb[j], sc, 0, 0, 0);
+    float sv[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (Tl.valid >> (4 * grp + r)) & 1;
+      sv[r] = ok ? sc[r] * a.qscale : -INFINITY;
+      mt = fmaxf(mt, sv[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const bool raise = __ballot(col < G && mt > m_ref + RESCALE_T) != 0;
+    if (raise) {
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+      l_run *= alpha;
+      m_ref = mn;
+      if (grp == 0 && col < G) pt[TILE][col] = alpha;
+    }
+    const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sv[r] - ms);
+      psum += p;
+      if (col < G) pt[4 * grp + r][col] = p;
+    }
+    l_run += psum;
+    wave_lds_sync();
+    if (raise) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const float al = pt[TILE][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+      }
+    }
+    const bool full = Tl.valid == ~0ull;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      float vx[8];
+      bf16x8_to_f32(Tl.v[ii], vx);
+      if (!full && !((Tl.valid >> (grp + 4 * ii)) & 1)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vx[e] = 0.f;
+      }
+      const float* prow = pt[grp + 4 * ii];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const float p = prow[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
+      }
+    }
+    wave_lds_sync();
+    const bool seg_last = c.k == c.tiles - 1;
+    if (seg_last || i == n - 1) end_segment(c, seg_last && started_here);
+  };
+
+  // ---- pipeline: table entry 3 tiles ahead, K/V 2 tiles ahead, compute ------------------
+  Cur cl = cc, ct = cc;  // load cursor, table cursor
+  int jl = 0, jt = 0;    // their tile indices within the range
+  auto adv_t = [&]() { advance(ct, jt < n - 1); jt += jt < n - 1; };
+  auto adv_l = [&]() { advance(cl, jl < n - 1); jl += jl < n - 1; };
+  Tile A, Bt, C;
+  int e_next = table_entry(ct);
+  adv_t();
+  int e_use = e_next;
+  e_next = table_entry(ct);
+  load_tile(cl, e_use, A);
+  adv_l();
+  adv_t();
+  e_use = e_next;
+  e_next = table_entry(ct);
+  load_tile(cl, e_use, Bt);
+  adv_l();
+  adv_t();
+  for (int i = 0; i < n; i += 3) {
+    e_use = e_next;
+    e_next = table_entry(ct);
+    load_tile(cl, e_use, C);
+    adv_l();
+    adv_t();
+    compute(A, cc, i);
+    advance(cc, i + 1 < n);
+    e_use = e_next;
+    e_next = table_entry(ct);
+    load_tile(cl, e_use, A);
+    adv_l();
+    adv_t();
+    if (i + 1 < n) {
+      compute(Bt, cc, i + 1);
+      advance(cc, i + 2 < n);
+    }
+    e_use = e_next;
+    e_next = table_entry(ct);
+    load_tile(cl, e_use, Bt);
+    adv_l();
+    adv_t();
+    if (i + 2 < n) {
+      compute(C, cc, i + 2);
+      advance(cc, i + 3 < n);
+    }
+  }
+}
+
+// Combines the partials of segments cut between wavefronts (one block per wavefront
+// whose range opens a cut segment: it holds the first piece, the following wavefronts
+// hold the rest in slot 0), and zeroes the output rows of empty sequences.
+__global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a) {
+  const int Hkv = a.kv_heads, G = a.group;
+  const int W = a.total_waves;
+  const int k1 = blockIdx.x;
+  if (k1 >= W) {
+    // zero rows: blocks W .. W + num_seqs - 1, one per sequence
+    const int s = k1 - W;
+    if (a.ws_cum[s + 1] != a.ws_cum[s]) return;
+    float* out = a.out + (size_t)s * a.q_heads * HD;
+    for (int i = threadIdx.x; i < a.q_heads * HD; i += blockDim.x) out[i] = 0.f;
+    return;
+  }
+  const int4 rec = reinterpret_cast<const int4*>(a.ws_rec)[k1];
+  if (rec.x < 0) return;
+  const int s = rec.x / Hkv, g = rec.x % Hkv;
+  const int seg_end = rec.z;
+  int k2 = k1;
+  while (k2 + 1 < W && a.ws_wave_start[k2 + 1] < seg_end) ++k2;
+  float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
+    const int h = i / HD, d = i % HD;
+    float M = -INFINITY;
+    for (int k = k1; k <= k2; ++k) {
+      const size_t pi = (size_t)k * 2 + (k == k1 ? rec.y : 0);
+      M = fmaxf(M, a.ws_ml[(pi * GSTRIDE + h) * 2]);
+    }
+    float den = 0.f, num = 0.f;
+    if (M != -INFINITY) {
+      for (int k = k1; k <= k2; ++k) {
+        const size_t pi = (size_t)k * 2 + (k == k1 ? rec.y : 0);
+        const float f = exp2f(a.ws_ml[(pi * GSTRIDE + h) * 2] - M);
+        den += f * a.ws_ml[(pi * GSTRIDE + h) * 2 + 1];
+        num += f * a.ws_acc[(pi * GSTRIDE + h) * HD + d];
+      }
+    }
+    out[(size_t)h * HD + d] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs) {
+  return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 && page_size > 0 &&
+         (page_size & (page_size - 1)) == 0 && num_seqs >= 1 && num_seqs <= BMAX;
+}
+
+// Workspace: per wavefront two partial slots of GSTRIDE heads and a merge record, then
+// the per-sequence prefix sums, then the first tile of every wavefront's range.
+inline size_t workspace_bytes(int total_waves, int num_seqs) {
+  const size_t slots = (size_t)total_waves * 2 * GSTRIDE;
+  return slots * 2 * sizeof(float) + slots * HD * sizeof(float) + (size_t)total_waves * 16 +
+         (size_t)(num_seqs + 1) * 4 + (size_t)total_waves * 4 + 256;
+}
+
+inline int launch(const DecodeArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)(a.total_waves / NW);
+  if (a.group <= 4)
+    hipLaunchKernelGGL(decode_stream_kernel<4>, dim3(blocks), dim3(64 * NW), 0, st, a);
+  else if (a.group <= 8)
+    hipLaunchKernelGGL(decode_stream_kernel<8>, dim3(blocks), dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_stream_kernel<16>, dim3(blocks), dim3(64 * NW), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)), dim3(128),
+                     0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace stream
+}  // namespace pa

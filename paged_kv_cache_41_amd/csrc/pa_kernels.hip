@@ -24,6 +24,7 @@
 #include "pa.h"
 #include "pa_common.hpp"
 #include "pa_decode_mfma.hpp"
+#include "pa_decode_stream.hpp"
 
 namespace pa {
 
@@ -283,6 +284,11 @@ DecodeFn pick_generic_d(int head_dim, int group) {
 
 inline int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 
+// Wavefronts of the streaming decode: one workgroup of four per compute unit of a 256-CU
+// MI355X, so the whole grid is resident at once (a second workgroup per unit measured
+// slower: more concurrent streams, each with less of its own data in flight).
+constexpr int stream_waves_max = 1024;
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Rows per chunk: a power of two between 16 and 512, about one eighth of the longest
@@ -392,6 +398,49 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
 
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
   DecodeArgs a{};
+  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs)) {
+    // balanced streaming path: wavefronts sized to the largest possible tile list
+    const int64_t tiles_max = (int64_t)num_seqs * kv_heads * ((max_live + 15) / 16 + 1);
+    int64_t waves = tiles_max / 8;
+    if (waves > stream_waves_max) waves = stream_waves_max;
+    if (waves < stream::NW) waves = stream::NW;
+    waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
+    const size_t need = stream::workspace_bytes((int)waves, num_seqs);
+    if (!workspace) {
+      *workspace_bytes = need;
+      return PA_OK;
+    }
+    if (*workspace_bytes < need) return PA_EWORKSPACE;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_EINVAL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+        !aligned16(workspace))
+      return PA_EUNSUPPORTED;
+    if ((int64_t)kv_heads * head_dim * 2 * page_size > UINT32_MAX) return PA_EUNSUPPORTED;
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.bt_stride = bt_stride;
+    a.ctx = context_lens;
+    a.num_seqs = num_seqs;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.group = group;
+    a.num_pages = num_pages;
+    a.page_size = page_size;
+    a.window = window > 0 ? window : 0;
+    a.max_ctx = max_context_len;
+    a.qscale = scale * 1.4426950408889634f;
+    a.total_waves = (int)waves;
+    const size_t slots = (size_t)waves * 2 * stream::GSTRIDE;
+    a.ws_ml = reinterpret_cast<float*>(workspace);
+    a.ws_acc = a.ws_ml + slots * 2;
+    a.ws_rec = reinterpret_cast<int*>(a.ws_acc + slots * stream::HD);
+    a.ws_cum = a.ws_rec + 4 * waves;
+    a.ws_wave_start = a.ws_cum + num_seqs + 1;
+    return stream::launch(a, reinterpret_cast<hipStream_t>(stream)) == 0 ? PA_OK : PA_ELAUNCH;
+  }
   a.chunk = pick_chunk(max_live);
   const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
   if (fast) a.chunk = mfma::chunk_for(num_seqs, kv_heads, max_live);
