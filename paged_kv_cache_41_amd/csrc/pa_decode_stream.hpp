@@ -17,12 +17,23 @@
 // pool and masked out of the softmax and P.V; past the end of the range the last tile
 // is re-read (a cache hit).
 //
-// Compute per tile is the matrix-core score tile (K as the A operand of four
-// v_mfma_f32_16x16x32_bf16, the group's queries as the B operand), base-2 online
-// softmax with a lazily raised reference max, and P.V in fp32 on the vector ALUs from
-// 16-byte column blocks of V.  A segment that starts and ends inside one wavefront
-// writes its output directly; the first and last segment of a range may be cut and
-// are written as partial (max, sum, accumulator) to one of two slots of that
+// Compute per tile runs on the matrix cores twice.  Scores: four
+// v_mfma_f32_16x16x32_bf16 with the K tile as the A operand (row = token, lane l holds
+// 64 contiguous bytes of token l % 16; the sum over head_dim is order-free, so lane
+// group l / 16 takes head_dim slice [32 (l / 16), +32)) and the group's queries as the
+// B operand (column = query head), leaving lane l with the scores of query head l % 16
+// for tokens 4 (l / 16) .. +3.  Softmax in base 2 with a lazily raised reference max
+// then gives each lane the probabilities of exactly those four tokens for its head,
+// which is the A-operand layout of v_mfma_f32_16x16x16_bf16 (row = head, k = token).
+// V is loaded so that lane l holds 16 contiguous bytes (8 columns) of tokens
+// 4 (l / 16) + j, j = 0..3, at column block l % 16; for each of the 8 columns e of the
+// block, v_perm_b32 gathers the four tokens' elements into the B operand (k = token,
+// n = column block), so eight P.V products cover all 128 columns with no LDS traffic.
+// The probabilities are split into a bf16 high part and a bf16 remainder and both are
+// multiplied, so P keeps about 16 significant bits (a bf16 P alone is not accurate
+// enough); the accumulators are fp32.  A segment that starts and ends inside one
+// wavefront writes its output directly; the first and last segment of a range may be
+// cut and are written as partial (max, sum, accumulator) to one of two slots of that
 // wavefront, which the merge kernel combines in a fixed order.
 #pragma once
 
@@ -39,23 +50,31 @@ namespace stream {
 
 using mfma::as_bf16x8;
 using mfma::bf16x8;
-using mfma::bf16x8_to_f32;
 using mfma::f32x4;
-using mfma::wave_lds_sync;
+
+typedef short bf16x4 __attribute__((ext_vector_type(4)));   // four bf16 as the MFMA takes them
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 128;
 constexpr int TILE = 16;
 constexpr int NW = 4;           // wavefronts per workgroup
 constexpr int BMAX = 2048;      // sequences handled by this path
-constexpr int PROW = 20;
 constexpr int GSTRIDE = 16;     // heads per partial slot
 constexpr float RESCALE_T = 8.f;
 
 struct Tile {
-  uint4 k[4];
-  uint4 v[4];
-  uint64_t valid;
+  uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
+  uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
+  uint64_t valid;    // bit t: token t0 + t is attended and mapped
 };
+
+// Two floats rounded to bf16 (nearest even) and packed, low element first.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2v h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // Position of a tile in the flattened list, with the fields of its segment.
 struct Cur {
@@ -67,12 +86,10 @@ struct Cur {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <int GMAX>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   __shared__ int s_cum[BMAX + 1];   // tiles of sequences before s
   __shared__ int s_len[BMAX];       // clamped context length
   __shared__ int s_scan[64 * NW];
-  __shared__ float s_p[NW][TILE + 1][PROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,8 +210,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
                                           ((uint32_t)(t & (P - 1)) * row_bytes + lane_off));
   };
 
-  // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + grp + 4 i (16 B at
-  // column block col); e = table entry of token t0 + col
+  // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + 4 grp + j (16 B
+  // at column block col); e = table entry of token t0 + col
   auto load_tile = [&](const Cur& c, int e, Tile& Tl) {
     const int t0 = c.t0base + c.k * TILE;
     const int tk = t0 + col;
@@ -205,20 +222,22 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ev = __shfl(e, grp + 4 * i, 64);
-      const int tv = min(max(t0 + grp + 4 * i, c.lo), c.L - 1);
-      Tl.v[i] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
+    for (int j = 0; j < 4; ++j) {
+      const int ev = __shfl(e, 4 * grp + j, 64);
+      const int tv = min(max(t0 + 4 * grp + j, c.lo), c.L - 1);
+      Tl.v[j] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
     }
   };
 
   // ---- per-segment state -----------------------------------------------------------------
+  // m_ref: reference max of score column col (query head col), the same in every lane
+  // group; l_run: this lane's share of the running sum (its four tokens); oacc[e][r]:
+  // output of query head 4 grp + r at column 8 col + e.
   bf16x8 qb[4];
   float m_ref = -INFINITY, l_run = 0.f;
-  float acc[GMAX][8];
+  f32x4 oacc[8];
   bool first_seg = true;     // the segment being computed is the first of this range
   bool started_here = false; // ... and this wavefront computed its tile 0
-  float(*pt)[PROW] = s_p[w];
 
   auto begin_segment = [&](const Cur& c) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
@@ -237,9 +256,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     m_ref = -INFINITY;
     l_run = 0.f;
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     started_here = c.k == 0;
   };
 
@@ -247,46 +264,44 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     float lt = l_run;
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
+    float lr[4];
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[h][e] += __shfl_xor(acc[h][e], 16, 64);
-        acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
-      }
+    for (int r = 0; r < 4; ++r) lr[r] = __shfl(lt, 4 * grp + r, 64);
     if (complete) {
       float* out = a.out + ((size_t)c.s * a.q_heads + (size_t)c.g * G) * HD + col * 8;
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        const float lh = __shfl(lt, h, 64);
-        if (h < G && lane < 16) {
-          const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;
           float4* o = reinterpret_cast<float4*>(out + (size_t)h * HD);
-          o[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-          o[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+          o[0] = make_float4(oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv);
+          o[1] = make_float4(oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv);
         }
       }
     } else {
-      const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
-      if (started_here && lane == 0) {
-        // this wavefront holds the first piece of a segment cut at its range end: leave
-        // the merge kernel a record (segment, slot of this piece, flattened end)
-        int4* rec = reinterpret_cast<int4*>(a.ws_rec);
-        rec[kw] = make_int4(c.s * Hkv + c.g, first_seg ? 0 : 1, seg_end_flat(c), 0);
-      }
+      const int slot = first_seg ? 0 : 1;
+      const size_t pi = (size_t)kw * 2 + slot;
       if (lane < G) {
         a.ws_ml[(pi * GSTRIDE + lane) * 2] = m_ref;
         a.ws_ml[(pi * GSTRIDE + lane) * 2 + 1] = lt;
       }
-      if (lane < 16) {
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-          if (h < G) {
-            float4* o = reinterpret_cast<float4*>(a.ws_acc + (pi * GSTRIDE + h) * HD + col * 8);
-            o[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-            o[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          float4* o = reinterpret_cast<float4*>(a.ws_acc + (pi * GSTRIDE + h) * HD + col * 8);
+          o[0] = make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]);
+          o[1] = make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]);
         }
+      }
+      if (started_here && lane == 0) {
+        // this wavefront holds the first piece of a segment cut at its range end: leave
+        // the merge kernel a record (segment, slot of this piece, wavefront of the last
+        // piece: the one whose range holds the segment's last tile)
+        const int64_t seg_end = seg_end_flat(c);
+        const int k2 = (int)((seg_end * W - 1) / T);
+        reinterpret_cast<int4*>(a.ws_rec)[kw] = make_int4(c.s * Hkv + c.g, slot, k2, 0);
       }
     }
     first_seg = false;
@@ -294,6 +309,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   auto compute = [&](const Tile& Tl, const Cur& c, int i) {
     if (i == 0 || c.k == 0) begin_segment(c);
+    // scores S[token][head] = K . q
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -308,50 +324,47 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const bool raise = __ballot(col < G && mt > m_ref + RESCALE_T) != 0;
-    if (raise) {
+    // raise the reference when some head's tile max passes it by more than RESCALE_T
+    if (__ballot(col < G && mt > m_ref + RESCALE_T) != 0) {
       const float mn = fmaxf(m_ref, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
       l_run *= alpha;
       m_ref = mn;
-      if (grp == 0 && col < G) pt[TILE][col] = alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[e][r] *= ar;
+      }
     }
     const float ms = m_ref == -INFINITY ? 0.f : m_ref;
-    float psum = 0.f;
+    float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sv[r] - ms);
-      psum += p;
-      if (col < G) pt[4 * grp + r][col] = p;
+      p[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - ms) : 0.f;
+      l_run += p[r];
     }
-    l_run += psum;
-    wave_lds_sync();
-    if (raise) {
+    // P as the A operand (row = head col, k = token 4 grp + r), split into a bf16 high
+    // part and the bf16-rounded remainder
+    const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+    const uint32_t l01 = pack_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
+    const bf16x4 plo = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
+    const uint32_t v0[4] = {Tl.v[0].x, Tl.v[0].y, Tl.v[0].z, Tl.v[0].w};
+    const uint32_t v1[4] = {Tl.v[1].x, Tl.v[1].y, Tl.v[1].z, Tl.v[1].w};
+    const uint32_t v2[4] = {Tl.v[2].x, Tl.v[2].y, Tl.v[2].z, Tl.v[2].w};
+    const uint32_t v3[4] = {Tl.v[3].x, Tl.v[3].y, Tl.v[3].z, Tl.v[3].w};
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        const float al = pt[TILE][h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-      }
+    for (int e = 0; e < 8; ++e) {
+      // column 8 col + e of the four tokens: the B operand (k = token, n = column block)
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
+      const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, oacc[e], 0, 0, 0);
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, oacc[e], 0, 0, 0);
     }
-    const bool full = Tl.valid == ~0ull;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float vx[8];
-      bf16x8_to_f32(Tl.v[ii], vx);
-      if (!full && !((Tl.valid >> (grp + 4 * ii)) & 1)) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vx[e] = 0.f;
-      }
-      const float* prow = pt[grp + 4 * ii];
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        const float p = prow[h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vx[e], acc[h][e]);
-      }
-    }
-    wave_lds_sync();
     const bool seg_last = c.k == c.tiles - 1;
     if (seg_last || i == n - 1) end_segment(c, seg_last && started_here);
   };
@@ -421,25 +434,23 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a) {
   const int4 rec = reinterpret_cast<const int4*>(a.ws_rec)[k1];
   if (rec.x < 0) return;
   const int s = rec.x / Hkv, g = rec.x % Hkv;
-  const int seg_end = rec.z;
-  int k2 = k1;
-  while (k2 + 1 < W && a.ws_wave_start[k2 + 1] < seg_end) ++k2;
+  const int k2 = rec.z;
   float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
   for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
     const int h = i / HD, d = i % HD;
-    float M = -INFINITY;
+    // one pass, pieces in order: running max, rescaled sum and accumulator
+    float M = -INFINITY, den = 0.f, num = 0.f;
     for (int k = k1; k <= k2; ++k) {
       const size_t pi = (size_t)k * 2 + (k == k1 ? rec.y : 0);
-      M = fmaxf(M, a.ws_ml[(pi * GSTRIDE + h) * 2]);
-    }
-    float den = 0.f, num = 0.f;
-    if (M != -INFINITY) {
-      for (int k = k1; k <= k2; ++k) {
-        const size_t pi = (size_t)k * 2 + (k == k1 ? rec.y : 0);
-        const float f = exp2f(a.ws_ml[(pi * GSTRIDE + h) * 2] - M);
-        den += f * a.ws_ml[(pi * GSTRIDE + h) * 2 + 1];
-        num += f * a.ws_acc[(pi * GSTRIDE + h) * HD + d];
-      }
+      const float m = a.ws_ml[(pi * GSTRIDE + h) * 2];
+      const float l = a.ws_ml[(pi * GSTRIDE + h) * 2 + 1];
+      const float x = a.ws_acc[(pi * GSTRIDE + h) * HD + d];
+      if (m == -INFINITY) continue;
+      const float mn = fmaxf(M, m);
+      const float fo = exp2f(M - mn), fn = exp2f(m - mn);
+      den = den * fo + l * fn;
+      num = num * fo + x * fn;
+      M = mn;
     }
     out[(size_t)h * HD + d] = den > 0.f ? num / den : 0.f;
   }
@@ -460,12 +471,7 @@ inline size_t workspace_bytes(int total_waves, int num_seqs) {
 
 inline int launch(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.total_waves / NW);
-  if (a.group <= 4)
-    hipLaunchKernelGGL(decode_stream_kernel<4>, dim3(blocks), dim3(64 * NW), 0, st, a);
-  else if (a.group <= 8)
-    hipLaunchKernelGGL(decode_stream_kernel<8>, dim3(blocks), dim3(64 * NW), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_stream_kernel<16>, dim3(blocks), dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL(decode_stream_kernel, dim3(blocks), dim3(64 * NW), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)), dim3(128),
                      0, st, a);
