@@ -65,7 +65,7 @@ constexpr float RESCALE_T = 8.f;
 struct Tile {
   uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
   uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
-  uint64_t valid;    // bit t: token t0 + t is attended and mapped
+  uint64_t valid;    // bit t (t < 16): token t0 + t is attended and mapped
 };
 
 // Two floats rounded to bf16 (nearest even) and packed, low element first.
@@ -212,10 +212,34 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + 4 grp + j (16 B
   // at column block col); e = table entry of token t0 + col
+  // Per-lane byte offsets that do not change from tile to tile when a tile lies inside one
+  // page (page size >= 16: tiles start at multiples of 16): K of token col, V of tokens
+  // 4 grp + j.
+  const bool page_tiles = P >= TILE;
+  const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 64;
+  const uint32_t v_lane_off = (uint32_t)(4 * grp) * row_bytes + col * 16;
+
   auto load_tile = [&](const Cur& c, int e, Tile& Tl) {
     const int t0 = c.t0base + c.k * TILE;
+    if (page_tiles) {
+      // one page for the whole tile: a uniform base address plus constant lane offsets
+      const int pg = uni(e);
+      const bool mapped = pg >= 0 && pg <= last_page;
+      const int lo_off = max(c.lo - t0, 0), hi_off = min(c.L - t0, TILE);
+      const uint32_t bits = ((1u << hi_off) - 1u) & ~((1u << lo_off) - 1u);
+      Tl.valid = mapped ? (uint64_t)bits : 0ull;
+      const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
+                            (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)c.g * HD * 2;
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
+      const char* vb = vbase + base + v_lane_off;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
+      return;
+    }
     const int tk = t0 + col;
-    Tl.valid = __ballot(tk >= c.lo && tk < c.L && e >= 0 && e <= last_page);
+    Tl.valid = __ballot(tk >= c.lo && tk < c.L && e >= 0 && e <= last_page) & 0xffffull;
     const uint32_t hoff = (uint32_t)c.g * HD * 2;
     const int tkc = min(max(tk, c.lo), c.L - 1);
     const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 64);
@@ -322,10 +346,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       sv[r] = ok ? sc[r] * a.qscale : -INFINITY;
       mt = fmaxf(mt, sv[r]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // raise the reference when some head's tile max passes it by more than RESCALE_T
+    // raise the reference when some head's tile max passes it by more than RESCALE_T;
+    // this lane's own max decides whether any does, so the cross-lane max is only taken
+    // on the (rare) raise
     if (__ballot(col < G && mt > m_ref + RESCALE_T) != 0) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float mn = fmaxf(m_ref, mt);
       const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
       l_run *= alpha;
@@ -351,10 +377,19 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
     const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
     const bf16x4 plo = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
-    const uint32_t v0[4] = {Tl.v[0].x, Tl.v[0].y, Tl.v[0].z, Tl.v[0].w};
-    const uint32_t v1[4] = {Tl.v[1].x, Tl.v[1].y, Tl.v[1].z, Tl.v[1].w};
-    const uint32_t v2[4] = {Tl.v[2].x, Tl.v[2].y, Tl.v[2].z, Tl.v[2].w};
-    const uint32_t v3[4] = {Tl.v[3].x, Tl.v[3].y, Tl.v[3].z, Tl.v[3].w};
+    // Rows outside the attended range get probability 0, but their V may be anything
+    // (rows of the last page past the sequence end are never written): replace them by
+    // zeros, since 0 * NaN would poison the product.
+    uint4 vt[4] = {Tl.v[0], Tl.v[1], Tl.v[2], Tl.v[3]};
+    if (Tl.valid != 0xffffull) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!((Tl.valid >> (4 * grp + j)) & 1)) vt[j] = make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
+    const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
+    const uint32_t v2[4] = {vt[2].x, vt[2].y, vt[2].z, vt[2].w};
+    const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // column 8 col + e of the four tokens: the B operand (k = token, n = column block)
@@ -419,7 +454,10 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 // Combines the partials of segments cut between wavefronts (one block per wavefront
 // whose range opens a cut segment: it holds the first piece, the following wavefronts
 // hold the rest in slot 0), and zeroes the output rows of empty sequences.
-__global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a) {
+constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_BATCH = 8;   // pieces whose partials are loaded together
+
+__global__ __launch_bounds__(MERGE_THREADS) void merge_stream_kernel(DecodeArgs a) {
   const int Hkv = a.kv_heads, G = a.group;
   const int W = a.total_waves;
   const int k1 = blockIdx.x;
@@ -434,23 +472,33 @@ __global__ __launch_bounds__(128) void merge_stream_kernel(DecodeArgs a) {
   const int4 rec = reinterpret_cast<const int4*>(a.ws_rec)[k1];
   if (rec.x < 0) return;
   const int s = rec.x / Hkv, g = rec.x % Hkv;
-  const int k2 = rec.z;
+  const int np = rec.z - k1 + 1;  // pieces: wavefronts k1 .. k2
   float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
   for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
     const int h = i / HD, d = i % HD;
-    // one pass, pieces in order: running max, rescaled sum and accumulator
+    // running max, rescaled sum and accumulator over the pieces in order; the loads of a
+    // batch of pieces are independent and issued together
     float M = -INFINITY, den = 0.f, num = 0.f;
-    for (int k = k1; k <= k2; ++k) {
-      const size_t pi = (size_t)k * 2 + (k == k1 ? rec.y : 0);
-      const float m = a.ws_ml[(pi * GSTRIDE + h) * 2];
-      const float l = a.ws_ml[(pi * GSTRIDE + h) * 2 + 1];
-      const float x = a.ws_acc[(pi * GSTRIDE + h) * HD + d];
-      if (m == -INFINITY) continue;
-      const float mn = fmaxf(M, m);
-      const float fo = exp2f(M - mn), fn = exp2f(m - mn);
-      den = den * fo + l * fn;
-      num = num * fo + x * fn;
-      M = mn;
+    for (int p0 = 0; p0 < np; p0 += MERGE_BATCH) {
+      float mm[MERGE_BATCH], ll[MERGE_BATCH], xx[MERGE_BATCH];
+#pragma unroll
+      for (int q = 0; q < MERGE_BATCH; ++q) {
+        const int p = p0 + q;
+        const size_t pi = (size_t)(k1 + p) * 2 + (p == 0 ? rec.y : 0);
+        const bool ok = p < np;
+        mm[q] = ok ? a.ws_ml[(pi * GSTRIDE + h) * 2] : -INFINITY;
+        ll[q] = ok ? a.ws_ml[(pi * GSTRIDE + h) * 2 + 1] : 0.f;
+        xx[q] = ok ? a.ws_acc[(pi * GSTRIDE + h) * HD + d] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < MERGE_BATCH; ++q) {
+        if (mm[q] == -INFINITY) continue;
+        const float mn = fmaxf(M, mm[q]);
+        const float fo = exp2f(M - mn), fn = exp2f(mm[q] - mn);
+        den = den * fo + ll[q] * fn;
+        num = num * fo + xx[q] * fn;
+        M = mn;
+      }
     }
     out[(size_t)h * HD + d] = den > 0.f ? num / den : 0.f;
   }
@@ -473,8 +521,8 @@ inline int launch(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.total_waves / NW);
   hipLaunchKernelGGL(decode_stream_kernel, dim3(blocks), dim3(64 * NW), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)), dim3(128),
-                     0, st, a);
+  hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)),
+                     dim3(MERGE_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -114,6 +114,12 @@ EDGE = {
     "page64_window": dict(q_heads=8, kv_heads=8, head_dim=128, page_size=64, window=100, len_lo=1, len_hi=900),
     "group3": dict(q_heads=6, kv_heads=2, head_dim=128, len_lo=1, len_hi=500),
     "group12_long": dict(num_seqs=3, q_heads=24, kv_heads=2, head_dim=128, len_lo=1500, len_hi=6000),
+    # rows of mapped pages that hold no data are NaN: masked rows must never reach a product
+    "nan_spare_p16": dict(q_heads=8, kv_heads=2, head_dim=128, len_lo=1, len_hi=300, spare="nan"),
+    "nan_spare_window": dict(q_heads=8, kv_heads=2, head_dim=128, window=37, len_lo=1, len_hi=400, spare="nan"),
+    "nan_spare_p1": dict(q_heads=8, kv_heads=2, head_dim=128, page_size=1, len_lo=0, len_hi=300, spare="nan"),
+    "nan_spare_p64": dict(q_heads=16, kv_heads=4, head_dim=128, page_size=64, window=70, len_lo=1, len_hi=700, spare="nan"),
+    "nan_spare_generic_f32": dict(q_heads=4, kv_heads=2, head_dim=64, dtype="f32", page_size=4, window=5, len_lo=1, len_hi=90, spare="nan"),
 }
 
 

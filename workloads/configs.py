@@ -18,9 +18,10 @@ Placement: the pages a scenario needs are taken from a seeded permutation of
 ``range(pool_pages)`` in (shared prefix, then sequence by sequence, then the
 copy targets) order.  Rows that are mapped but hold no data (the slots of the
 new row before the write, slots past ``L`` in the last page, rows of the first
-live page that lie before the window) hold large finite canaries; pages that
-no table maps hold NaN.  A kernel that attends a masked row therefore gives a
-gross error, and one that reads an unmapped page gives NaN.
+live page that lie before the window) hold large finite canaries, or NaN with
+``spare="nan"``; pages that no table maps hold NaN.  A kernel that attends a
+masked row therefore gives a gross error (canaries) or NaN, and one that reads
+an unmapped page gives NaN.
 
 Random values are float32 N(0, 1) drawn with a seeded ``torch.Generator`` on
 the requested device and rounded to the pool dtype (round to nearest even);
@@ -66,6 +67,7 @@ class Spec:
     slot_table: bool = False       # raw token-slot table, page-size-1 addressing
     slot_stride: int = 0           # width of the slot table; 0: align32(longest context)
     scale: float = 0.0             # 0: fp32(1/sqrt(head_dim))
+    spare: str = "canary"          # rows of mapped pages that hold no data: "canary" or "nan"
 
 
 def _align32(x: int) -> int:
@@ -166,6 +168,12 @@ def _draw_lens(spec: Spec, rng: np.random.Generator) -> np.ndarray:
     raise ValueError(spec.len_dist)
 
 
+def spare_is_canary(spec: Spec) -> bool:
+    if spec.spare not in ("canary", "nan"):
+        raise ValueError(spec.spare)
+    return spec.spare == "canary"
+
+
 def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False) -> Scenario:
     """Build the scenario of ``spec`` with ``seed`` on ``device``."""
     rng = np.random.default_rng(seed)
@@ -221,9 +229,9 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
     def randn(*shape):
         return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32).to(tdt)
 
-    # every mapped page first gets canaries, then the rows that hold data
+    # every mapped page first gets canaries (or stays NaN), then the rows that hold data
     mapped = sorted({p for m in seq_pages for p in m.values()})
-    if mapped:
+    if mapped and spare_is_canary(spec):
         idx = torch.tensor(mapped, device=device, dtype=torch.long)
         k_pool[idx] = K_CANARY
         v_pool[idx] = V_CANARY
