@@ -7,8 +7,15 @@ through the C ABI on one stream, with every input resident in HBM.  The
 default workload is the batch-64 GQA decode (32 q / 8 kv heads, head_dim 128,
 pages of 16 rows, context lengths uniform in [1, 4096], bf16).
 
+By default every timed step starts cold: a 1 GiB read first evicts the K/V
+from L2 and from the 256 MB last-level cache, so the attended rows come from
+HBM as they would between two layers of a model; step and decode times are then
+taken with HIP events on the launch stream.  The same number of back-to-back
+steps (where part of one step's K/V is still cached for the next) is reported
+beside it.
+
 Prints one JSON line: effective KV GB/s of the step (attended K/V bytes per
-step / step time), the decode launch's own time and its fraction of HBM peak
+step / step time), the decode call's own time and its fraction of HBM peak
 from HIP events on the launch stream, and the CPU oracle timed on a bounded
 sample of the same batch.
 """
@@ -33,14 +40,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     p.add_argument("--seed", type=int, default=None)
-    p.add_argument("--flush", action="store_true",
-                   help="overwrite a 512 MiB buffer before each step (outside the events)")
+    p.add_argument("--warm-steps", type=int, default=None,
+                   help="also time this many back-to-back steps without a flush "
+                        "(default: --steps; 0: skip)")
+    p.add_argument("--flush", choices=["none", "read", "write"], default="read",
+                   help="before each step (outside the events) read (clean eviction) or "
+                        "overwrite a 1 GiB buffer, so no K/V row is still in the 256 MB "
+                        "last-level cache")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--traffic", type=str, default=None,
-                   help="JSON file with measured HBM bytes per decode launch")
+    p.add_argument("--traffic", type=str,
+                   default=os.path.join(ROOT, "profiles", "decode_gqa_b64_hbm_traffic.md"),
+                   help="counter summary holding the measured HBM bytes per decode call")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip the device-to-device copy reference measurement")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.warm_steps is None:
+        a.warm_steps = a.steps if a.flush != "none" else 0
+    return a
 
 
 def decode_bytes(sc) -> dict:
@@ -74,6 +90,36 @@ def unique_kv_bytes(sc) -> int:
     rows_per = P if P > 1 else 1
     # rows of each distinct page that some sequence attends (approximate at page grain)
     return len(seen) * rows_per * 2 * s.kv_heads * s.head_dim * elt
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the HIP sources the library is built from (names and contents)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_41_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(path: str, workload: str):
+    """HBM bytes per decode call from a committed counter summary, if it covers this
+    workload and was taken on the current kernel sources; else None."""
+    if not path or not os.path.exists(path) or workload != "gqa_b64":
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "|", "#")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
@@ -163,8 +209,18 @@ def main():
                                       sc.context_lens, window=s.window,
                                       max_context_len=sc.max_context_len)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+    flush = None
+    if args.flush != "none":
+        flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
+
+    def do_flush():
+        if args.flush == "write":
+            flush.fill_(1)
+        else:
+            flush.sum(dtype=torch.int64)
     stream = torch.cuda.current_stream(dev)
+    nb = decode_bytes(sc)
+    kv_bytes_step = nb["kv"]
 
     def step():
         ops.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
@@ -180,38 +236,63 @@ def main():
         attend()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # warm: K steps back to back (the K/V of one step partly survives in the 256 MB
+    # last-level cache for the next)
+    warm = None
+    if args.warm_steps > 0:
+        wev = [ev_pair() for _ in range(args.warm_steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warm_steps):
+            step()
+            wev[i][0].record(stream)
+            attend()
+            wev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wwall = time.perf_counter() - t0
+        wdec = float(np.mean([a.elapsed_time(b) for a, b in wev]))
+        warm = {"steps": args.warm_steps, "ms_per_step": round(wwall / args.warm_steps * 1e3, 5),
+                "decode_avg_us": round(wdec * 1e3, 2),
+                "kv_gbps": round(kv_bytes_step / (wwall / args.warm_steps) / 1e9, 1),
+                "decode_kv_gbps": round(kv_bytes_step / (wdec * 1e-3) / 1e9, 1)}
+
+    # timed: K steps; with a flush, each step starts with the K/V evicted from every
+    # cache and is timed on the stream with events
+    ev = [ev_pair() for _ in range(args.steps)]
+    sev = [ev_pair() for _ in range(args.steps)]
     wall = 0.0
     if flush is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
+            sev[i][0].record(stream)
             step()
             ev[i][0].record(stream)
             attend()
             ev[i][1].record(stream)
+            sev[i][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        ms_step = wall / args.steps * 1e3
     else:
+        torch.cuda.synchronize()
         for i in range(args.steps):
-            flush.zero_()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
+            do_flush()
+            sev[i][0].record(stream)
             step()
             ev[i][0].record(stream)
             attend()
             ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            wall += time.perf_counter() - t0
+            sev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_step = float(np.mean([a.elapsed_time(b) for a, b in sev]))
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    ms_step = wall / args.steps * 1e3
-    nb = decode_bytes(sc)
     dec_avg = float(dec_ms.mean())
     achieved = nb["total"] / (dec_avg * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(s.name)
+    traffic = measured_traffic(args.traffic, s.name)
     result = {
         "metric": "paged decode attention effective KV GB/s (% HBM peak) + seqs/s",
         "value": round(nb["kv"] / (ms_step * 1e-3) / 1e9, 2),
@@ -230,18 +311,26 @@ def main():
                    "window": s.window, "seed": sc.seed, "context_sum": int(sc.lens.sum()),
                    "kv_bytes_per_step": nb["kv"], "copies": int(len(sc.copy_src)),
                    "stored_rows": int((sc.slot_mapping >= 0).sum()),
-                   "flush_between_steps": bool(args.flush)},
+                   "cache": ("cold: every timed step starts after a 1 GiB read that evicts "
+                             "the K/V from L2 and the 256 MB last-level cache; step and decode "
+                             "times from HIP events on the launch stream")
+                            if args.flush == "read" else
+                            ("back-to-back steps" if args.flush == "none" else
+                             "every step starts after a 1 GiB write")},
         "seqs_per_s": round(s.num_seqs / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * nb["kv"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "decode": {"avg_us": round(dec_avg * 1e3, 2), "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                    "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                    "kv_gbps": round(nb["kv"] / (dec_avg * 1e-3) / 1e9, 1),
                    "seqs_per_s": round(s.num_seqs / (dec_avg * 1e-3), 1)},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (split + merge launches)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "pa_decode call: decode_stream_kernel + merge_stream_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": nb["total"]},
     }
+    if warm is not None:
+        result["warm_back_to_back"] = warm
     if s.prefix_len:
         result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
     if not args.no_copy_ceiling:
