@@ -61,6 +61,9 @@ constexpr int NW = 4;           // wavefronts per workgroup
 constexpr int BMAX = 2048;      // sequences handled by this path
 constexpr int GSTRIDE = 16;     // heads per partial slot
 constexpr float RESCALE_T = 8.f;
+#ifndef STREAM_DEPTH
+#define STREAM_DEPTH 2   // tiles of K/V in flight per wavefront while one is computed
+#endif
 
 struct Tile {
   uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
@@ -86,6 +89,7 @@ struct Cur {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+template <int DEPTH, bool PAGE_TILES>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   __shared__ int s_cum[BMAX + 1];   // tiles of sequences before s
   __shared__ int s_len[BMAX];       // clamped context length
@@ -200,9 +204,21 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     }
   };
 
+  // Table entries.  With pages of at least 16 rows the tile lies in one page: one entry,
+  // read through the scalar path (constant address space), whose completion is counted
+  // apart from the vector loads, so waiting for it never drains the K/V tiles in flight.
+  // Smaller pages need one entry per token (lane col holds token t0 + col's).
+  const __attribute__((address_space(4))) int32_t* bt_const =
+      (const __attribute__((address_space(4))) int32_t*)a.block_tables;
   auto table_entry = [&](const Cur& c) {
-    const int t = min(max(c.t0base + c.k * TILE + col, c.lo), c.L - 1);
-    return a.block_tables[(size_t)c.s * a.bt_stride + (t >> lp)];
+    if constexpr (PAGE_TILES) {
+      const int t = min(max(c.t0base + c.k * TILE, c.lo), c.L - 1);
+      // num_seqs * bt_stride < 2^31 on this path, so the index fits one scalar register
+      return bt_const[uni(c.s * a.bt_stride + (t >> lp))];
+    } else {
+      const int t = min(max(c.t0base + c.k * TILE + col, c.lo), c.L - 1);
+      return a.block_tables[(size_t)c.s * a.bt_stride + (t >> lp)];
+    }
   };
 
   auto row_addr = [&](const char* base, int pg, int t, uint32_t lane_off) {
@@ -215,13 +231,13 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // Per-lane byte offsets that do not change from tile to tile when a tile lies inside one
   // page (page size >= 16: tiles start at multiples of 16): K of token col, V of tokens
   // 4 grp + j.
-  const bool page_tiles = P >= TILE;
+  constexpr bool page_tiles = PAGE_TILES;
   const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 64;
   const uint32_t v_lane_off = (uint32_t)(4 * grp) * row_bytes + col * 16;
 
   auto load_tile = [&](const Cur& c, int e, Tile& Tl) {
     const int t0 = c.t0base + c.k * TILE;
-    if (page_tiles) {
+    if constexpr (page_tiles) {
       // one page for the whole tile: a uniform base address plus constant lane offsets
       const int pg = uni(e);
       const bool mapped = pg >= 0 && pg <= last_page;
@@ -404,49 +420,36 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     if (seg_last || i == n - 1) end_segment(c, seg_last && started_here);
   };
 
-  // ---- pipeline: table entry 3 tiles ahead, K/V 2 tiles ahead, compute ------------------
+  // ---- pipeline: table entry DEPTH+1 tiles ahead, K/V DEPTH tiles ahead, compute ------
+  // The K/V buffers form a ring of DEPTH+1 tiles indexed by compile-time constants (the
+  // inner loop is fully unrolled), so every stage keeps fixed registers.
   Cur cl = cc, ct = cc;  // load cursor, table cursor
   int jl = 0, jt = 0;    // their tile indices within the range
   auto adv_t = [&]() { advance(ct, jt < n - 1); jt += jt < n - 1; };
   auto adv_l = [&]() { advance(cl, jl < n - 1); jl += jl < n - 1; };
-  Tile A, Bt, C;
+  Tile buf[DEPTH + 1];
   int e_next = table_entry(ct);
   adv_t();
-  int e_use = e_next;
-  e_next = table_entry(ct);
-  load_tile(cl, e_use, A);
-  adv_l();
-  adv_t();
-  e_use = e_next;
-  e_next = table_entry(ct);
-  load_tile(cl, e_use, Bt);
-  adv_l();
-  adv_t();
-  for (int i = 0; i < n; i += 3) {
-    e_use = e_next;
+#pragma unroll
+  for (int u = 0; u < DEPTH; ++u) {
+    const int e_use = e_next;
     e_next = table_entry(ct);
-    load_tile(cl, e_use, C);
-    adv_l();
     adv_t();
-    compute(A, cc, i);
-    advance(cc, i + 1 < n);
-    e_use = e_next;
-    e_next = table_entry(ct);
-    load_tile(cl, e_use, A);
+    load_tile(cl, e_use, buf[u]);
     adv_l();
-    adv_t();
-    if (i + 1 < n) {
-      compute(Bt, cc, i + 1);
-      advance(cc, i + 2 < n);
-    }
-    e_use = e_next;
-    e_next = table_entry(ct);
-    load_tile(cl, e_use, Bt);
-    adv_l();
-    adv_t();
-    if (i + 2 < n) {
-      compute(C, cc, i + 2);
-      advance(cc, i + 3 < n);
+  }
+  for (int i = 0; i < n; i += DEPTH + 1) {
+#pragma unroll
+    for (int u = 0; u <= DEPTH; ++u) {
+      const int e_use = e_next;
+      e_next = table_entry(ct);
+      adv_t();
+      load_tile(cl, e_use, buf[(u + DEPTH) % (DEPTH + 1)]);
+      adv_l();
+      if (i + u < n) {
+        compute(buf[u], cc, i + u);
+        advance(cc, i + u + 1 < n);
+      }
     }
   }
 }
@@ -504,9 +507,11 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_stream_kernel(DecodeArgs 
   }
 }
 
-inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs) {
+inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs,
+                     int bt_stride) {
   return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 && page_size > 0 &&
-         (page_size & (page_size - 1)) == 0 && num_seqs >= 1 && num_seqs <= BMAX;
+         (page_size & (page_size - 1)) == 0 && num_seqs >= 1 && num_seqs <= BMAX &&
+         (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31);
 }
 
 // Workspace: per wavefront two partial slots of GSTRIDE heads and a merge record, then
@@ -519,7 +524,12 @@ inline size_t workspace_bytes(int total_waves, int num_seqs) {
 
 inline int launch(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.total_waves / NW);
-  hipLaunchKernelGGL(decode_stream_kernel, dim3(blocks), dim3(64 * NW), 0, st, a);
+  if (a.page_size >= TILE)
+    hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true>), dim3(blocks), dim3(64 * NW), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false>), dim3(blocks), dim3(64 * NW),
+                       0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)),
                      dim3(MERGE_THREADS), 0, st, a);

@@ -398,7 +398,7 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
 
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
   DecodeArgs a{};
-  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs)) {
+  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride)) {
     // balanced streaming path: wavefronts sized to the largest possible tile list
     const int64_t tiles_max = (int64_t)num_seqs * kv_heads * ((max_live + 15) / 16 + 1);
     int64_t waves = tiles_max / 8;
