@@ -208,7 +208,7 @@ def main():
     need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
                                       sc.context_lens, window=s.window,
                                       max_context_len=sc.max_context_len)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     flush = None
     if args.flush != "none":
         flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)

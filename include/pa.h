@@ -114,8 +114,11 @@ int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_pages,
  *   attended rows, with fp32 accumulation.
  *   workspace     device scratch of *workspace_bytes bytes.  With workspace ==
  *                 NULL the call only stores the required size in
- *                 *workspace_bytes and returns PA_OK.  The contents need no
- *                 initialization and are not meaningful after the call.
+ *                 *workspace_bytes and returns PA_OK.  It must hold zeros
+ *                 before its first use (it carries counters that the kernel
+ *                 counts up and puts back to zero); every completed call
+ *                 leaves it ready for the next one, whatever the shapes.
+ *                 Calls that overlap in time must not share a workspace.
  *   Supported: dtype PA_F32 or PA_BF16; head_dim 16, 32, 64, 128 or 256;
  *   q_heads / kv_heads <= 16; any page_size >= 1.
  */

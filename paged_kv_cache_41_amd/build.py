@@ -21,6 +21,9 @@ OUT = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep uniform-address atomics as written: the optimizer's rewrite reads the
+         # result right after the atomic, which drains every load in flight
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -21,9 +21,7 @@ struct DecodeArgs {
   float qscale;                // scale * log2(e): logits are kept in base 2
   float* ws_ml;                // partial running max and running sum, pairs
   float* ws_acc;               // partial accumulators, head_dim floats each
-  int* ws_cum;                 // streaming path: per-sequence tile prefix sums
-  int* ws_wave_start;          // streaming path: first tile of each wavefront's range
-  int* ws_rec;                 // streaming path: per-wavefront merge records (4 ints)
+  int* ws_arrive;              // streaming path: per-range arrival counters, zero between calls
   int total_waves;             // streaming path: wavefronts sharing the tile list
 };
 

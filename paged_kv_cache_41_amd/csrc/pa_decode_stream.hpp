@@ -59,8 +59,8 @@ constexpr int HD = 128;
 constexpr int TILE = 16;
 constexpr int NW = 4;           // wavefronts per workgroup
 constexpr int BMAX = 2048;      // sequences handled by this path
-constexpr int GSTRIDE = 16;     // heads per partial slot
 constexpr float RESCALE_T = 8.f;
+constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
 #ifndef STREAM_DEPTH
 #define STREAM_DEPTH 2   // tiles of K/V in flight per wavefront while one is computed
 #endif
@@ -68,6 +68,8 @@ constexpr float RESCALE_T = 8.f;
 struct Tile {
   uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
   uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
+  uint4 q[4];        // query head lane % 16, bytes [64 (lane / 16), +64): loaded with the
+                     // tile that opens a segment piece only
   uint64_t valid;    // bit t (t < 16): token t0 + t is attended and mapped
 };
 
@@ -89,12 +91,116 @@ struct Cur {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Device-scope (relaxed) accesses for data handed between wavefronts of one launch.
+__device__ __forceinline__ void dev_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float dev_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- ranges of the flattened tile list ---------------------------------------------------
+// With T tiles in the list and W wavefronts, the first R = min(W, T) wavefronts take one
+// range each: range r is [r T / R, (r + 1) T / R), never empty.  Range order is list order,
+// so the pieces of a segment cut by range boundaries lie in consecutive ranges.
+__device__ __forceinline__ int range_start(int T, int R, int r) {
+  return (int)((int64_t)r * T / R);
+}
+// the range holding tile x
+__device__ __forceinline__ int range_of(int T, int R, int x) {
+  return (int)(((int64_t)(x + 1) * R - 1) / T);
+}
+
+// What the load and compute stages need of one tile.
+enum : int {
+  RANGE_FIRST = 1,   // first tile of the range
+  RANGE_LAST = 2,    // last tile of the range
+  SEG_FIRST = 4,     // tile 0 of its segment
+  SEG_LAST = 8,      // last tile of its segment
+  IDLE = 16,         // past the end of the range: loaded (a repeat) but not computed
+};
+struct Desc {
+  int s, g;          // sequence, kv head
+  int t0;            // first row of the tile
+  int lo, L;         // attended rows [lo, L) of the sequence
+  int flags;
+};
+
+// Per-sequence tile prefix sums and clamped lengths, built by every workgroup at the start.
+__shared__ int st_cum[BMAX + 1];   // tiles of sequences before s (st_cum[B] = all)
+__shared__ int st_len[BMAX];       // clamped context length
+__shared__ int st_scan[64 * NW];
+
+// The front of a wavefront's pipeline: walks its range one tile per step, then stays on
+// the last tile, marked idle.
+struct Front {
+  Cur f;
+  int rem;            // tiles of the range from the front on (1: the front is on its last)
+  bool first;         // the front is on the first tile of the range
+  bool idle;
+  int B, Hkv, window;
+
+  __device__ __forceinline__ void seg_fields() {
+    f.tiles = uni(st_cum[f.s + 1] - st_cum[f.s]);
+    f.L = uni(st_len[f.s]);
+    f.lo = (window > 0 && f.L > window) ? f.L - window : 0;
+    f.t0base = (f.lo >> 4) << 4;
+  }
+  // position of flattened tile x
+  __device__ __forceinline__ void locate(int x) {
+    int lo_s = 0, hi_s = B - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (Hkv * st_cum[mid] <= x) lo_s = mid; else hi_s = mid - 1;
+    }
+    f.s = uni(lo_s);
+    seg_fields();
+    const int within = x - Hkv * st_cum[f.s];
+    f.g = uni(within / f.tiles);
+    f.k = uni(within % f.tiles);
+  }
+  // next tile of the list; one is known to follow (segments of empty sequences are skipped)
+  __device__ __forceinline__ void step() {
+    if (f.k + 1 < f.tiles) {
+      f.k += 1;
+      return;
+    }
+    f.k = 0;
+    f.g += 1;
+    if (f.g == Hkv) {
+      f.g = 0;
+      int s = f.s;
+      do { s += 1; } while (st_cum[s + 1] == st_cum[s]);
+      f.s = uni(s);
+      seg_fields();
+    }
+  }
+  __device__ __forceinline__ Desc desc() const {
+    Desc d;
+    d.s = f.s;
+    d.g = f.g;
+    d.t0 = f.t0base + f.k * TILE;
+    d.lo = f.lo;
+    d.L = f.L;
+    d.flags = idle ? IDLE
+                   : ((first ? RANGE_FIRST : 0) | (rem == 1 ? RANGE_LAST : 0) |
+                      (f.k == 0 ? SEG_FIRST : 0) | (f.k == f.tiles - 1 ? SEG_LAST : 0));
+    return d;
+  }
+  __device__ __forceinline__ void next() {
+    if (idle) return;
+    first = false;
+    if (rem > 1) {
+      step();
+      rem -= 1;
+    } else {
+      idle = true;
+    }
+  }
+};
+
 template <int DEPTH, bool PAGE_TILES>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
-  __shared__ int s_cum[BMAX + 1];   // tiles of sequences before s
-  __shared__ int s_len[BMAX];       // clamped context length
-  __shared__ int s_scan[64 * NW];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -112,45 +218,45 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         int L, lo, n;
         live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
         const int t = n > 0 ? ((L - 1) >> 4) - (lo >> 4) + 1 : 0;
-        s_len[s] = L;
-        s_cum[s] = t;
+        st_len[s] = L;
+        st_cum[s] = t;
         local += t;
       }
     }
-    s_scan[tid] = local;
+    st_scan[tid] = local;
     __syncthreads();
     for (int off = 1; off < 64 * NW; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
+      const int v = tid >= off ? st_scan[tid - off] : 0;
       __syncthreads();
-      s_scan[tid] += v;
+      st_scan[tid] += v;
       __syncthreads();
     }
-    int run = tid > 0 ? s_scan[tid - 1] : 0;
+    int run = tid > 0 ? st_scan[tid - 1] : 0;
     for (int i = 0; i < per; ++i) {
       const int s = tid * per + i;
       if (s < B) {
-        const int t = s_cum[s];
-        s_cum[s] = run;
+        const int t = st_cum[s];
+        st_cum[s] = run;
         run += t;
       }
     }
-    if (tid == 0) s_cum[B] = s_scan[64 * NW - 1];
+    if (tid == 0) st_cum[B] = st_scan[64 * NW - 1];
     __syncthreads();
-    if (blockIdx.x == 0)
-      for (int i = tid; i <= B; i += 64 * NW) a.ws_cum[i] = s_cum[i];
+  }
+  // output rows of sequences with nothing to attend are zero
+  for (int s = blockIdx.x; s < B; s += gridDim.x) {
+    if (st_cum[s + 1] != st_cum[s]) continue;
+    float* out = a.out + (size_t)s * a.q_heads * HD;
+    for (int i = tid; i < a.q_heads * HD; i += 64 * NW) out[i] = 0.f;
   }
 
-  // ---- this wavefront's range of tiles ----------------------------------------------------
-  const int64_t T = (int64_t)Hkv * s_cum[B];
-  const int W = a.total_waves;
+  // ---- this wavefront's range ------------------------------------------------------------
+  const int T = uni(Hkv * st_cum[B]);
+  const int R = min(a.total_waves, T);
   const int kw = blockIdx.x * NW + w;
-  const int ta = (int)((int64_t)kw * T / W);
-  const int n = (int)((int64_t)(kw + 1) * T / W) - ta;
-  if (lane == 0) {
-    a.ws_wave_start[kw] = ta;
-    reinterpret_cast<int4*>(a.ws_rec)[kw] = make_int4(-1, 0, 0, 0);
-  }
-  if (n <= 0) return;
+  if (kw >= R) return;
+  const int ta = range_start(T, R, kw);
+  const int n = range_start(T, R, kw + 1) - ta;
 
   const int P = a.page_size;
   const int lp = 31 - __clz(P);
@@ -162,47 +268,14 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  auto seg_fields = [&](Cur& c) {
-    c.tiles = uni(s_cum[c.s + 1] - s_cum[c.s]);
-    c.L = uni(s_len[c.s]);
-    c.lo = (a.window > 0 && c.L > a.window) ? c.L - a.window : 0;
-    c.t0base = (c.lo >> 4) << 4;
-  };
-  // one past the flattened index of the segment's last tile
-  auto seg_end_flat = [&](const Cur& c) {
-    return Hkv * s_cum[c.s] + (c.g + 1) * c.tiles;
-  };
-  // locate flattened tile ta
-  Cur cc;
-  {
-    int lo_s = 0, hi_s = B - 1;
-    while (lo_s < hi_s) {
-      const int mid = (lo_s + hi_s + 1) >> 1;
-      if ((int64_t)Hkv * s_cum[mid] <= ta) lo_s = mid; else hi_s = mid - 1;
-    }
-    cc.s = uni(lo_s);
-    seg_fields(cc);
-    const int within = ta - Hkv * s_cum[cc.s];
-    cc.g = uni(within / cc.tiles);
-    cc.k = uni(within % cc.tiles);
-  }
-  // advance to the next tile; `more` is false at the last tile of the range (the cursor
-  // then stays, so the stages re-read it)
-  auto advance = [&](Cur& c, bool more) {
-    if (!more) return;
-    if (c.k + 1 < c.tiles) {
-      c.k += 1;
-      return;
-    }
-    c.k = 0;
-    c.g += 1;
-    if (c.g == Hkv) {
-      c.g = 0;
-      do { c.s += 1; } while (s_cum[c.s + 1] == s_cum[c.s]);
-      c.s = uni(c.s);
-      seg_fields(c);
-    }
-  };
+  Front fr;
+  fr.B = B;
+  fr.Hkv = Hkv;
+  fr.window = a.window;
+  fr.locate(ta);
+  fr.rem = n;
+  fr.first = true;
+  fr.idle = false;
 
   // Table entries.  With pages of at least 16 rows the tile lies in one page: one entry,
   // read through the scalar path (constant address space), whose completion is counted
@@ -210,14 +283,14 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // Smaller pages need one entry per token (lane col holds token t0 + col's).
   const __attribute__((address_space(4))) int32_t* bt_const =
       (const __attribute__((address_space(4))) int32_t*)a.block_tables;
-  auto table_entry = [&](const Cur& c) {
+  auto table_entry = [&](const Desc& d) {
     if constexpr (PAGE_TILES) {
-      const int t = min(max(c.t0base + c.k * TILE, c.lo), c.L - 1);
+      const int t = min(max(d.t0, d.lo), d.L - 1);
       // num_seqs * bt_stride < 2^31 on this path, so the index fits one scalar register
-      return bt_const[uni(c.s * a.bt_stride + (t >> lp))];
+      return bt_const[uni(d.s * a.bt_stride + (t >> lp))];
     } else {
-      const int t = min(max(c.t0base + c.k * TILE + col, c.lo), c.L - 1);
-      return a.block_tables[(size_t)c.s * a.bt_stride + (t >> lp)];
+      const int t = min(max(d.t0 + col, d.lo), d.L - 1);
+      return a.block_tables[(size_t)d.s * a.bt_stride + (t >> lp)];
     }
   };
 
@@ -227,25 +300,31 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   };
 
   // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + 4 grp + j (16 B
-  // at column block col); e = table entry of token t0 + col
-  // Per-lane byte offsets that do not change from tile to tile when a tile lies inside one
-  // page (page size >= 16: tiles start at multiples of 16): K of token col, V of tokens
-  // 4 grp + j.
-  constexpr bool page_tiles = PAGE_TILES;
+  // at column block col).  When a tile lies inside one page (page size >= 16: tiles start
+  // at multiples of 16) the per-lane byte offsets are the same for every tile.
   const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 64;
   const uint32_t v_lane_off = (uint32_t)(4 * grp) * row_bytes + col * 16;
 
-  auto load_tile = [&](const Cur& c, int e, Tile& Tl) {
-    const int t0 = c.t0base + c.k * TILE;
-    if constexpr (page_tiles) {
+  auto load_tile = [&](const Desc& d, int e, Tile& Tl) {
+    const int t0 = d.t0;
+    if (d.flags & (RANGE_FIRST | SEG_FIRST)) {
+      // the query rows of the group, fetched with the tile so that waiting for them is
+      // waiting for this tile; lanes past the group read head 0 and are zeroed later
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(a.q) +
+          ((size_t)d.s * a.q_heads + (size_t)d.g * G + (col < G ? col : 0)) * HD + grp * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Tl.q[j] = qrow[j];
+    }
+    if constexpr (PAGE_TILES) {
       // one page for the whole tile: a uniform base address plus constant lane offsets
       const int pg = uni(e);
       const bool mapped = pg >= 0 && pg <= last_page;
-      const int lo_off = max(c.lo - t0, 0), hi_off = min(c.L - t0, TILE);
+      const int lo_off = max(d.lo - t0, 0), hi_off = min(d.L - t0, TILE);
       const uint32_t bits = ((1u << hi_off) - 1u) & ~((1u << lo_off) - 1u);
       Tl.valid = mapped ? (uint64_t)bits : 0ull;
       const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
-                            (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)c.g * HD * 2;
+                            (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)d.g * HD * 2;
       const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
@@ -255,16 +334,16 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       return;
     }
     const int tk = t0 + col;
-    Tl.valid = __ballot(tk >= c.lo && tk < c.L && e >= 0 && e <= last_page) & 0xffffull;
-    const uint32_t hoff = (uint32_t)c.g * HD * 2;
-    const int tkc = min(max(tk, c.lo), c.L - 1);
+    Tl.valid = __ballot(tk >= d.lo && tk < d.L && e >= 0 && e <= last_page) & 0xffffull;
+    const uint32_t hoff = (uint32_t)d.g * HD * 2;
+    const int tkc = min(max(tk, d.lo), d.L - 1);
     const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 64);
 #pragma unroll
     for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ev = __shfl(e, 4 * grp + j, 64);
-      const int tv = min(max(t0 + 4 * grp + j, c.lo), c.L - 1);
+      const int tv = min(max(t0 + 4 * grp + j, d.lo), d.L - 1);
       Tl.v[j] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
     }
   };
@@ -276,31 +355,25 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   bf16x8 qb[4];
   float m_ref = -INFINITY, l_run = 0.f;
   f32x4 oacc[8];
-  bool first_seg = true;     // the segment being computed is the first of this range
-  bool started_here = false; // ... and this wavefront computed its tile 0
+  bool first_seg = true;     // the segment being computed is the first of the range
+  bool started_here = false; // ... and its tile 0 lies in this range
+  // cut segments this range holds a piece of: its first segment (piece in slot 0) and its
+  // last (slot 1); segment index s * Hkv + g and the ranges of its first and last piece
+  bool cut0 = false, cut1 = false;
+  int seg0 = 0, k1_0 = 0, k2_0 = 0, seg1 = 0, k1_1 = 0, k2_1 = 0;
 
-  auto begin_segment = [&](const Cur& c) {
+  auto begin_segment = [&](const Desc& d, const Tile& Tl) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((size_t)c.s * a.q_heads + (size_t)c.g * G + (col < G ? col : 0)) * HD +
-                           grp * 32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * j);
-      qb[j] = as_bf16x8(col < G ? v : zero);
-    }
-    // Wait here, on this rare path, for the query rows: otherwise the compiler would
-    // have to assume the load may still be outstanding wherever the query registers
-    // are read and drain every prefetched tile before each tile's compute.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(col < G ? Tl.q[j] : zero);
     m_ref = -INFINITY;
     l_run = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    started_here = c.k == 0;
+    started_here = (d.flags & SEG_FIRST) != 0;
   };
 
-  auto end_segment = [&](const Cur& c, bool complete) {
+  auto end_segment = [&](const Desc& d, bool complete) {
     float lt = l_run;
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
@@ -308,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) lr[r] = __shfl(lt, 4 * grp + r, 64);
     if (complete) {
-      float* out = a.out + ((size_t)c.s * a.q_heads + (size_t)c.g * G) * HD + col * 8;
+      float* out = a.out + ((size_t)d.s * a.q_heads + (size_t)d.g * G) * HD + col * 8;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
@@ -320,35 +393,43 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         }
       }
     } else {
-      const int slot = first_seg ? 0 : 1;
-      const size_t pi = (size_t)kw * 2 + slot;
+      // a piece of a segment cut by a range boundary: partial (max, sum, accumulator) to
+      // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
+      // through to the point where every compute unit reads it)
+      const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
       if (lane < G) {
-        a.ws_ml[(pi * GSTRIDE + lane) * 2] = m_ref;
-        a.ws_ml[(pi * GSTRIDE + lane) * 2 + 1] = lt;
+        dev_store(a.ws_ml + (pi * G + lane) * 2, m_ref);
+        dev_store(a.ws_ml + (pi * G + lane) * 2 + 1, lt);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
-          float4* o = reinterpret_cast<float4*>(a.ws_acc + (pi * GSTRIDE + h) * HD + col * 8);
-          o[0] = make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]);
-          o[1] = make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]);
+          float* o = a.ws_acc + (pi * G + h) * HD + col * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dev_store(o + e, oacc[e][r]);
         }
       }
-      if (started_here && lane == 0) {
-        // this wavefront holds the first piece of a segment cut at its range end: leave
-        // the merge kernel a record (segment, slot of this piece, wavefront of the last
-        // piece: the one whose range holds the segment's last tile)
-        const int64_t seg_end = seg_end_flat(c);
-        const int k2 = (int)((seg_end * W - 1) / T);
-        reinterpret_cast<int4*>(a.ws_rec)[kw] = make_int4(c.s * Hkv + c.g, slot, k2, 0);
+      const int tiles = st_cum[d.s + 1] - st_cum[d.s];
+      const int seg_start = Hkv * st_cum[d.s] + d.g * tiles;
+      const int k1 = range_of(T, R, seg_start), k2 = range_of(T, R, seg_start + tiles - 1);
+      if (first_seg) {
+        cut0 = true;
+        seg0 = d.s * Hkv + d.g;
+        k1_0 = k1;
+        k2_0 = k2;
+      } else {
+        cut1 = true;
+        seg1 = d.s * Hkv + d.g;
+        k1_1 = k1;
+        k2_1 = k2;
       }
     }
     first_seg = false;
   };
 
-  auto compute = [&](const Tile& Tl, const Cur& c, int i) {
-    if (i == 0 || c.k == 0) begin_segment(c);
+  auto compute = [&](const Tile& Tl, const Desc& d) {
+    if (d.flags & (RANGE_FIRST | SEG_FIRST)) begin_segment(d, Tl);
     // scores S[token][head] = K . q
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -416,110 +497,148 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, oacc[e], 0, 0, 0);
       oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, oacc[e], 0, 0, 0);
     }
-    const bool seg_last = c.k == c.tiles - 1;
-    if (seg_last || i == n - 1) end_segment(c, seg_last && started_here);
+    if (d.flags & (SEG_LAST | RANGE_LAST))
+      end_segment(d, (d.flags & SEG_LAST) && started_here);
   };
 
   // ---- pipeline: table entry DEPTH+1 tiles ahead, K/V DEPTH tiles ahead, compute ------
-  // The K/V buffers form a ring of DEPTH+1 tiles indexed by compile-time constants (the
-  // inner loop is fully unrolled), so every stage keeps fixed registers.
-  Cur cl = cc, ct = cc;  // load cursor, table cursor
-  int jl = 0, jt = 0;    // their tile indices within the range
-  auto adv_t = [&]() { advance(ct, jt < n - 1); jt += jt < n - 1; };
-  auto adv_l = [&]() { advance(cl, jl < n - 1); jl += jl < n - 1; };
+  // The K/V buffers and their descriptors form a ring of DEPTH+1 slots indexed by
+  // compile-time constants (the inner loop is fully unrolled), so every stage keeps fixed
+  // registers.  Past the end of the range the front repeats its last tile marked IDLE: it
+  // is re-read (a cache hit) and skipped.
   Tile buf[DEPTH + 1];
-  int e_next = table_entry(ct);
-  adv_t();
+  Desc dsc[DEPTH + 1];
+  Desc d_next = fr.desc();
+  int e_next = table_entry(d_next);
+  fr.next();
 #pragma unroll
   for (int u = 0; u < DEPTH; ++u) {
+    const Desc d_use = d_next;
     const int e_use = e_next;
-    e_next = table_entry(ct);
-    adv_t();
-    load_tile(cl, e_use, buf[u]);
-    adv_l();
+    d_next = fr.desc();
+    e_next = table_entry(d_next);
+    fr.next();
+    load_tile(d_use, e_use, buf[u]);
+    dsc[u] = d_use;
   }
-  for (int i = 0; i < n; i += DEPTH + 1) {
+  for (;;) {
 #pragma unroll
     for (int u = 0; u <= DEPTH; ++u) {
+      const Desc d_use = d_next;
       const int e_use = e_next;
-      e_next = table_entry(ct);
-      adv_t();
-      load_tile(cl, e_use, buf[(u + DEPTH) % (DEPTH + 1)]);
-      adv_l();
-      if (i + u < n) {
-        compute(buf[u], cc, i + u);
-        advance(cc, i + u + 1 < n);
-      }
+      d_next = fr.desc();
+      e_next = table_entry(d_next);
+      fr.next();
+      load_tile(d_use, e_use, buf[(u + DEPTH) % (DEPTH + 1)]);
+      dsc[(u + DEPTH) % (DEPTH + 1)] = d_use;
+      if (!(dsc[u].flags & IDLE)) compute(buf[u], dsc[u]);
     }
+    if (dsc[DEPTH].flags & IDLE) break;
   }
+
+  // ---- cut segments: the piece that arrives last combines them ---------------------------
+  // Each piece counts itself on the counter of the segment's first range once its partial
+  // is written; the one that completes the count reads every piece's partial, combines
+  // them in range order, and puts the counter back to zero for the next call.  Partials
+  // and counters move only through device-scope accesses (stores written through, loads
+  // that skip the caches of the compute unit and of its die), and the count is raised only
+  // after this wavefront's partial stores have completed (vmcnt reaches 0), so a
+  // wavefront that sees the full count reads complete partials.  No cache-wide write-back
+  // or invalidate is needed: nothing is exchanged through ordinary cached stores.
+  if (!cut0 && !cut1) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: every store above has completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int arrived0 = 0, arrived1 = 0;
+  if (lane == 0) {
+    if (cut0)
+      arrived0 = __hip_atomic_fetch_add(a.ws_arrive + k1_0, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    if (cut1)
+      arrived1 = __hip_atomic_fetch_add(a.ws_arrive + k1_1, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+  }
+  arrived0 = __builtin_amdgcn_readlane(arrived0, 0);
+  arrived1 = __builtin_amdgcn_readlane(arrived1, 0);
+  const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
+  const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
+  if (!last0 && !last1) return;
+  // One wavefront combines a segment: lane l takes columns 4 (l % 32) .. +3 of heads
+  // l / 32, l / 32 + 2, ...; the partials of COMBINE_BATCH pieces are loaded together.
+  auto combine = [&](int seg, int k1, int k2) {
+    const int s = seg / Hkv, g = seg % Hkv;
+    const int tiles = st_cum[s + 1] - st_cum[s];
+    const int seg_start = Hkv * st_cum[s] + g * tiles;
+    // in range k1 the segment is the first one (slot 0) only if it starts the range
+    const int slot1 = seg_start == range_start(T, R, k1) ? 0 : 1;
+    float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
+    const int c4 = (lane & 31) * 4;
+    for (int h = lane >> 5; h < G; h += 2) {
+      float M = -INFINITY, den = 0.f;
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k0 = k1; k0 <= k2; k0 += COMBINE_BATCH) {
+        float2 ml[COMBINE_BATCH];
+        float4 x[COMBINE_BATCH];
+#pragma unroll
+        for (int b = 0; b < COMBINE_BATCH; ++b) {
+          const int k = min(k0 + b, k2);
+          const size_t pi = (size_t)k * 2 + (k == k1 ? slot1 : 0);
+          const float* pml = a.ws_ml + (pi * G + h) * 2;
+          const float* px = a.ws_acc + (pi * G + h) * HD + c4;
+          ml[b] = make_float2(dev_load(pml), dev_load(pml + 1));
+          x[b] = make_float4(dev_load(px), dev_load(px + 1), dev_load(px + 2), dev_load(px + 3));
+        }
+#pragma unroll
+        for (int b = 0; b < COMBINE_BATCH; ++b) {
+          const float mm = ml[b].x;
+          if (k0 + b > k2 || mm == -INFINITY) continue;
+          const float mn = fmaxf(M, mm);
+          const float fo = exp2f(M - mn), fn = exp2f(mm - mn);
+          den = den * fo + ml[b].y * fn;
+          num.x = num.x * fo + x[b].x * fn;
+          num.y = num.y * fo + x[b].y * fn;
+          num.z = num.z * fo + x[b].z * fn;
+          num.w = num.w * fo + x[b].w * fn;
+          M = mn;
+        }
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      *reinterpret_cast<float4*>(out + (size_t)h * HD + c4) =
+          make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    }
+    if (lane == 0)
+      __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (last0) combine(seg0, k1_0, k2_0);
+  if (last1) combine(seg1, k1_1, k2_1);
 }
 
-// Combines the partials of segments cut between wavefronts (one block per wavefront
-// whose range opens a cut segment: it holds the first piece, the following wavefronts
-// hold the rest in slot 0), and zeroes the output rows of empty sequences.
-constexpr int MERGE_THREADS = 256;
-constexpr int MERGE_BATCH = 8;   // pieces whose partials are loaded together
-
-__global__ __launch_bounds__(MERGE_THREADS) void merge_stream_kernel(DecodeArgs a) {
-  const int Hkv = a.kv_heads, G = a.group;
-  const int W = a.total_waves;
-  const int k1 = blockIdx.x;
-  if (k1 >= W) {
-    // zero rows: blocks W .. W + num_seqs - 1, one per sequence
-    const int s = k1 - W;
-    if (a.ws_cum[s + 1] != a.ws_cum[s]) return;
-    float* out = a.out + (size_t)s * a.q_heads * HD;
-    for (int i = threadIdx.x; i < a.q_heads * HD; i += blockDim.x) out[i] = 0.f;
-    return;
-  }
-  const int4 rec = reinterpret_cast<const int4*>(a.ws_rec)[k1];
-  if (rec.x < 0) return;
-  const int s = rec.x / Hkv, g = rec.x % Hkv;
-  const int np = rec.z - k1 + 1;  // pieces: wavefronts k1 .. k2
-  float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
-  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
-    const int h = i / HD, d = i % HD;
-    // running max, rescaled sum and accumulator over the pieces in order; the loads of a
-    // batch of pieces are independent and issued together
-    float M = -INFINITY, den = 0.f, num = 0.f;
-    for (int p0 = 0; p0 < np; p0 += MERGE_BATCH) {
-      float mm[MERGE_BATCH], ll[MERGE_BATCH], xx[MERGE_BATCH];
-#pragma unroll
-      for (int q = 0; q < MERGE_BATCH; ++q) {
-        const int p = p0 + q;
-        const size_t pi = (size_t)(k1 + p) * 2 + (p == 0 ? rec.y : 0);
-        const bool ok = p < np;
-        mm[q] = ok ? a.ws_ml[(pi * GSTRIDE + h) * 2] : -INFINITY;
-        ll[q] = ok ? a.ws_ml[(pi * GSTRIDE + h) * 2 + 1] : 0.f;
-        xx[q] = ok ? a.ws_acc[(pi * GSTRIDE + h) * HD + d] : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < MERGE_BATCH; ++q) {
-        if (mm[q] == -INFINITY) continue;
-        const float mn = fmaxf(M, mm[q]);
-        const float fo = exp2f(M - mn), fn = exp2f(mm[q] - mn);
-        den = den * fo + ll[q] * fn;
-        num = num * fo + xx[q] * fn;
-        M = mn;
-      }
-    }
-    out[(size_t)h * HD + d] = den > 0.f ? num / den : 0.f;
-  }
+// Tiles of the list at most: every segment covers ceil(n / 16) + 1 tiles at most.
+inline int64_t tiles_bound(int num_seqs, int kv_heads, int max_live) {
+  return (int64_t)num_seqs * kv_heads * ((max_live + 15) / 16 + 1);
 }
 
 inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs,
-                     int bt_stride) {
+                     int bt_stride, int kv_heads, int max_live) {
   return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 && page_size > 0 &&
          (page_size & (page_size - 1)) == 0 && num_seqs >= 1 && num_seqs <= BMAX &&
-         (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31);
+         (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31) &&
+         tiles_bound(num_seqs, kv_heads, max_live) < ((int64_t)1 << 30);
 }
 
-// Workspace: per wavefront two partial slots of GSTRIDE heads and a merge record, then
-// the per-sequence prefix sums, then the first tile of every wavefront's range.
-inline size_t workspace_bytes(int total_waves, int num_seqs) {
-  const size_t slots = (size_t)total_waves * 2 * GSTRIDE;
-  return slots * 2 * sizeof(float) + slots * HD * sizeof(float) + (size_t)total_waves * 16 +
-         (size_t)(num_seqs + 1) * 4 + (size_t)total_waves * 4 + 256;
+// Workspace: the arrival counters (zero between calls), then per wavefront two partial
+// slots of `group` heads (running max and sum, accumulator).
+inline size_t workspace_bytes(int total_waves, int group) {
+  const size_t slots = (size_t)total_waves * 2 * group;
+  const size_t counters = ((size_t)total_waves * 4 + 255) / 256 * 256;
+  return counters + slots * 2 * sizeof(float) + slots * HD * sizeof(float);
+}
+inline void carve_workspace(DecodeArgs& a, void* workspace) {
+  const size_t slots = (size_t)a.total_waves * 2 * a.group;
+  const size_t counters = ((size_t)a.total_waves * 4 + 255) / 256 * 256;
+  a.ws_arrive = reinterpret_cast<int*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counters);
+  a.ws_acc = a.ws_ml + slots * 2;
 }
 
 inline int launch(const DecodeArgs& a, hipStream_t st) {
@@ -530,9 +649,6 @@ inline int launch(const DecodeArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false>), dim3(blocks), dim3(64 * NW),
                        0, st, a);
-  if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(merge_stream_kernel, dim3((unsigned)(a.total_waves + a.num_seqs)),
-                     dim3(MERGE_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -398,14 +398,15 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
 
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
   DecodeArgs a{};
-  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride)) {
-    // balanced streaming path: wavefronts sized to the largest possible tile list
-    const int64_t tiles_max = (int64_t)num_seqs * kv_heads * ((max_live + 15) / 16 + 1);
+  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
+                       max_live)) {
+    // balanced streaming path: wavefronts and chunks sized to the largest possible list
+    const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live);
     int64_t waves = tiles_max / 8;
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
-    const size_t need = stream::workspace_bytes((int)waves, num_seqs);
+    const size_t need = stream::workspace_bytes((int)waves, group);
     if (!workspace) {
       *workspace_bytes = need;
       return PA_OK;
@@ -433,12 +434,7 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
     a.max_ctx = max_context_len;
     a.qscale = scale * 1.4426950408889634f;
     a.total_waves = (int)waves;
-    const size_t slots = (size_t)waves * 2 * stream::GSTRIDE;
-    a.ws_ml = reinterpret_cast<float*>(workspace);
-    a.ws_acc = a.ws_ml + slots * 2;
-    a.ws_rec = reinterpret_cast<int*>(a.ws_acc + slots * stream::HD);
-    a.ws_cum = a.ws_rec + 4 * waves;
-    a.ws_wave_start = a.ws_cum + num_seqs + 1;
+    stream::carve_workspace(a, workspace);
     return stream::launch(a, reinterpret_cast<hipStream_t>(stream)) == 0 ? PA_OK : PA_ELAUNCH;
   }
   a.chunk = pick_chunk(max_live);

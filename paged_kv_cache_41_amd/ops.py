@@ -111,6 +111,9 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
 
     A raw token-slot table is passed as ``block_tables`` together with pools
     viewed in pages of one row (``pool.view(-1, 1, kv_heads, head_dim)``).
+    A ``workspace`` passed in must be zero-filled before its first use; each call
+    leaves it ready for the next.  Without one (or with one too small) a zeroed
+    workspace is allocated for this call.
     """
     dev = _dev(q, k_pool, v_pool, block_tables, context_lens)
     n, P, hkv, d = _pool_dims(k_pool, v_pool)
@@ -130,7 +133,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, scale,
                         max_context_len, None, 0, None)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, scale,
                  max_context_len, workspace.data_ptr(),
                  workspace.numel() * workspace.element_size(), _stream(dev, stream))

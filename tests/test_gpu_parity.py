@@ -140,6 +140,63 @@ def test_full_table_context():
     check_step(sc)
 
 
+def test_short_contexts_under_large_bound():
+    # contexts far below max_context_len: the grid is sized for the bound, so most
+    # wavefronts find no work and the ranges of the others hold a tile or two, cutting
+    # segments into many pieces; the workspace was used before by a call of another shape
+    spec = workloads.Spec(name="short_under_bound", dtype="bf16", num_seqs=6, q_heads=32,
+                          kv_heads=8, head_dim=128, page_size=16, len_lo=1, len_hi=70,
+                          bt_stride=256, pool_factor=1.5)
+    sc = workloads.build(spec, 9, device="cuda")
+    print(f"case {spec.name}", flush=True)
+    o = ops()
+    kp0, vp0 = bits(sc.k_pool), bits(sc.v_pool)
+    o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    bound = 256 * 16
+    need = o.decode_workspace_bytes(sc.q, sc.k_pool, sc.v_pool, sc.block_tables,
+                                    sc.context_lens, max_context_len=bound)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    other = workloads.make_config(2, device="cuda", num_seqs=8)
+    assert o.decode_workspace_bytes(other.q, other.k_pool, other.v_pool, other.block_tables,
+                                    other.context_lens,
+                                    max_context_len=other.max_context_len) <= need
+    o.decode(other.q, other.k_pool, other.v_pool, other.block_tables, other.context_lens,
+             max_context_len=other.max_context_len, workspace=ws)
+    out = o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+                   scale=sc.scale, max_context_len=bound, workspace=ws)
+    torch.cuda.synchronize()
+    _, _, ref = expected_step(sc, k_pool_bits=kp0, v_pool_bits=vp0)
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    assert float(np.max(np.abs(got - ref))) <= TOL["bf16"]
+
+
+def test_workspace_reused_across_calls():
+    # the chunk ticket counter lives in the workspace: it must start over on every call
+    sc = workloads.make_config(2, device="cuda")
+    o = ops()
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    need = o.decode_workspace_bytes(sc.q, sc.k_pool, sc.v_pool, sc.block_tables,
+                                    sc.context_lens, max_context_len=sc.max_context_len)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    run = lambda: o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+                           scale=sc.scale, max_context_len=sc.max_context_len,
+                           workspace=ws).clone()
+    first = run()
+    for _ in range(3):
+        assert torch.equal(run(), first), "a call with a reused workspace differs"
+    small = workloads.make_config(2, device="cuda", num_seqs=5)
+    o.store_kv(small.k_pool, small.v_pool, small.k_new, small.v_new, small.slot_mapping)
+    got = o.decode(small.q, small.k_pool, small.v_pool, small.block_tables, small.context_lens,
+                   scale=small.scale, max_context_len=small.max_context_len, workspace=ws)
+    torch.cuda.synchronize()
+    _, _, ref = expected_step(small)
+    # expected_step replays copy and store on the already stored pools: identical rows
+    assert float(np.max(np.abs(got.cpu().double().numpy() - ref))) <= TOL["bf16"]
+    assert torch.equal(run(), first)
+
+
 def test_deterministic_and_placement_invariant():
     spec = workloads.config_spec(2)
     sc = workloads.build(spec, 77, device="cuda")
