@@ -324,7 +324,7 @@ def main():
                    "kv_gbps": round(nb["kv"] / (dec_avg * 1e-3) / 1e9, 1),
                    "seqs_per_s": round(s.num_seqs / (dec_avg * 1e-3), 1)},
         "roofline": {"bound": "hbm",
-                     "kernel": "pa_decode call: decode_stream_kernel + merge_stream_kernel",
+                     "kernel": "pa_decode call: decode_stream_kernel (one launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": nb["total"]},

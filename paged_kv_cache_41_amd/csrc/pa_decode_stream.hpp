@@ -91,13 +91,35 @@ struct Cur {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Device-scope (relaxed) accesses for data handed between wavefronts of one launch.
-__device__ __forceinline__ void dev_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float dev_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Device-scope accesses for the partials handed between wavefronts of one launch: buffer
+// instructions with the sc1 cache policy (stores written through to the point where every
+// compute unit reads them, loads that skip the caches of the compute unit and of its die),
+// 8 or 16 bytes per lane.  The descriptor covers the partial area only; the hardware
+// drops accesses past it.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int CPOL_DEVICE = 16;    // sc1
+struct DevBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ DevBuf(void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ void store4(uint32_t off, float4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0,
+                                           CPOL_DEVICE);
+  }
+  __device__ __forceinline__ void store2(uint32_t off, float2 v) const {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, (int)off, 0,
+                                          CPOL_DEVICE);
+  }
+  __device__ __forceinline__ float4 load4(uint32_t off) const {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0,
+                                                                            CPOL_DEVICE));
+  }
+  __device__ __forceinline__ float2 load2(uint32_t off) const {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0,
+                                                                           CPOL_DEVICE));
+  }
+};
 
 // ---- ranges of the flattened tile list ---------------------------------------------------
 // With T tiles in the list and W wavefronts, the first R = min(W, T) wavefronts take one
@@ -357,6 +379,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   f32x4 oacc[8];
   bool first_seg = true;     // the segment being computed is the first of the range
   bool started_here = false; // ... and its tile 0 lies in this range
+  // partial area: the (max, sum) pair of every slot and head, then their accumulators
+  const uint32_t nslots = (uint32_t)a.total_waves * 2 * G;
+  const DevBuf part(a.ws_ml, nslots * (2 + HD) * 4);
+  auto ml_off = [&](uint32_t idx) { return idx * 8; };
+  auto acc_off = [&](uint32_t idx) { return nslots * 8 + idx * HD * 4; };
   // cut segments this range holds a piece of: its first segment (piece in slot 0) and its
   // last (slot 1); segment index s * Hkv + g and the ranges of its first and last piece
   bool cut0 = false, cut1 = false;
@@ -397,17 +424,14 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
       // through to the point where every compute unit reads it)
       const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
-      if (lane < G) {
-        dev_store(a.ws_ml + (pi * G + lane) * 2, m_ref);
-        dev_store(a.ws_ml + (pi * G + lane) * 2 + 1, lt);
-      }
+      if (lane < G) part.store2(ml_off((uint32_t)pi * G + lane), make_float2(m_ref, lt));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
-          float* o = a.ws_acc + (pi * G + h) * HD + col * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dev_store(o + e, oacc[e][r]);
+          const uint32_t o = acc_off((uint32_t)pi * G + h) + col * 32;
+          part.store4(o, make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]));
+          part.store4(o + 16, make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]));
         }
       }
       const int tiles = st_cum[d.s + 1] - st_cum[d.s];
@@ -583,10 +607,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
           const size_t pi = (size_t)k * 2 + (k == k1 ? slot1 : 0);
-          const float* pml = a.ws_ml + (pi * G + h) * 2;
-          const float* px = a.ws_acc + (pi * G + h) * HD + c4;
-          ml[b] = make_float2(dev_load(pml), dev_load(pml + 1));
-          x[b] = make_float4(dev_load(px), dev_load(px + 1), dev_load(px + 2), dev_load(px + 3));
+          ml[b] = part.load2(ml_off((uint32_t)pi * G + h));
+          x[b] = part.load4(acc_off((uint32_t)pi * G + h) + c4 * 4);
         }
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
