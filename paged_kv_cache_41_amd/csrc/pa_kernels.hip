@@ -402,7 +402,9 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
                        max_live)) {
     // balanced streaming path: wavefronts and chunks sized to the largest possible list
     const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live);
-    int64_t waves = tiles_max / 8;
+    // about 22 tiles per wavefront at least (so the start-up and the end of a range stay
+    // small next to its stream), at most stream_waves_max
+    int64_t waves = tiles_max / 22;
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
