@@ -89,6 +89,19 @@ def test_config_slot_table_sampled():
     check_step(sc, seqs=seqs)
 
 
+@pytest.mark.parametrize("window", [0, 40])
+def test_batch_above_streaming_limit(window):
+    # more sequences than the streaming path takes: the chunked matrix-core path
+    spec = workloads.Spec(name=f"b2100_w{window}", dtype="bf16", num_seqs=2100, q_heads=16,
+                          kv_heads=4, head_dim=128, page_size=16, window=window, len_lo=1,
+                          len_hi=300, pool_factor=1.25)
+    sc = workloads.build(spec, 13, device="cuda")
+    rng = np.random.default_rng(2)
+    seqs = sorted(set(rng.choice(2100, 40, replace=False).tolist()) |
+                  {0, 2099, int(np.argmax(sc.lens)), int(np.argmin(sc.lens))})
+    check_step(sc, seqs=seqs)
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_random_small(seed):
     sc = workloads.build(workloads.random_spec(seed), seed, device="cuda")
