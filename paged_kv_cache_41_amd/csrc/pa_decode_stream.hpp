@@ -151,7 +151,7 @@ struct Desc {
 // Per-sequence tile prefix sums and clamped lengths, built by every workgroup at the start.
 __shared__ int st_cum[BMAX + 1];   // tiles of sequences before s (st_cum[B] = all)
 __shared__ int st_len[BMAX];       // clamped context length
-__shared__ int st_scan[64 * NW];
+__shared__ int st_scan[NW];       // wavefront totals of the scan
 
 // The front of a wavefront's pipeline: walks its range one tile per step, then stays on
 // the last tile, marked idle.
@@ -245,15 +245,18 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         local += t;
       }
     }
-    st_scan[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < 64 * NW; off <<= 1) {
-      const int v = tid >= off ? st_scan[tid - off] : 0;
-      __syncthreads();
-      st_scan[tid] += v;
-      __syncthreads();
+    // inclusive scan within the wavefront (shuffles), then the wavefront totals in LDS
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-    int run = tid > 0 ? st_scan[tid - 1] : 0;
+    if (lane == 63) st_scan[w] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += st_scan[i];
+    int run = base + incl - local;
     for (int i = 0; i < per; ++i) {
       const int s = tid * per + i;
       if (s < B) {
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         run += t;
       }
     }
-    if (tid == 0) st_cum[B] = st_scan[64 * NW - 1];
+    if (tid == 64 * NW - 1) st_cum[B] = base + incl;
     __syncthreads();
   }
   // output rows of sequences with nothing to attend are zero
