@@ -21,6 +21,12 @@ at logical row ``L - 1``):
    Maps to tiny-llm".)
 
 ``L == 0`` yields a zero output row.
+
+Attention sinks (silicon-compiler chapter 15, section "Exercises", exercise 3):
+with ``S`` sink rows and a window ``W`` the step attends the first ``S`` rows
+and the last ``W - S`` rows, so the context is still ``W`` rows once ``L``
+exceeds ``W``; while ``L <= W`` every row is attended.  ``0 <= S < W`` keeps
+the new token among the attended rows.
 """
 from __future__ import annotations
 
@@ -36,6 +42,29 @@ def live_rows(L: int, window: int) -> tuple[int, int]:
     if window > 0:
         return L - min(L, window), L
     return 0, L
+
+
+def attended_rows(L: int, window: int, sinks: int = 0) -> list:
+    """Logical rows attended by a sequence of ``L`` rows, in increasing order."""
+    if window <= 0 or sinks <= 0:
+        lo, hi = live_rows(L, window)
+        return list(range(lo, hi))
+    if not sinks < window:
+        raise ValueError(f"{sinks} sink rows need a window of more than {sinks} rows")
+    lo, hi = live_rows(L, window - sinks)
+    return sorted(set(range(min(sinks, L))) | set(range(lo, hi)))
+
+
+def gather_rows(pool_bits: np.ndarray, table_row: np.ndarray, rows, dtype: str) -> np.ndarray:
+    """Logical rows ``rows`` of one sequence through its block table, in float64."""
+    num_pages, P = pool_bits.shape[0], pool_bits.shape[1]
+    out = np.empty((len(rows),) + pool_bits.shape[2:], dtype=np.float64)
+    for n, i in enumerate(rows):
+        page = int(table_row[i // P])
+        if not 0 <= page < num_pages:
+            raise IndexError(f"row {i} maps to page {page}, outside the pool of {num_pages}")
+        out[n] = to_f64(pool_bits[page, i % P], dtype)
+    return out
 
 
 def gather(pool_bits: np.ndarray, table_row: np.ndarray, lo: int, hi: int,
@@ -70,12 +99,12 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
 def decode(q_bits: np.ndarray, k_pool_bits: np.ndarray, v_pool_bits: np.ndarray,
            block_tables: np.ndarray, context_lens: np.ndarray, page_size: int,
            window: int, scale: float, dtype: str,
-           seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+           seqs: Optional[Iterable[int]] = None, sinks: int = 0) -> np.ndarray:
     """Float64 output ``[len(seqs), q_heads, head_dim]`` of one decode step.
 
     ``q_bits`` is ``[num_seqs, q_heads, head_dim]`` raw bits; ``block_tables``
     is ``[>= num_seqs, stride]`` integers; ``seqs`` selects sequences (all by
-    default).
+    default); ``sinks`` rows at the start are kept besides the window.
     """
     assert k_pool_bits.shape[1] == page_size and v_pool_bits.shape == k_pool_bits.shape
     num_seqs, q_heads, head_dim = q_bits.shape
@@ -89,9 +118,14 @@ def decode(q_bits: np.ndarray, k_pool_bits: np.ndarray, v_pool_bits: np.ndarray,
             raise ValueError(f"negative context length {L}")
         if L == 0:
             continue
-        lo, hi = live_rows(L, window)
-        K = gather(k_pool_bits, block_tables[s], lo, hi, dtype)
-        V = gather(v_pool_bits, block_tables[s], lo, hi, dtype)
+        if sinks > 0 and window > 0:
+            rows = attended_rows(L, window, sinks)
+            K = gather_rows(k_pool_bits, block_tables[s], rows, dtype)
+            V = gather_rows(v_pool_bits, block_tables[s], rows, dtype)
+        else:
+            lo, hi = live_rows(L, window)
+            K = gather(k_pool_bits, block_tables[s], lo, hi, dtype)
+            V = gather(v_pool_bits, block_tables[s], lo, hi, dtype)
         qs = to_f64(q_bits[s], dtype)
         for h in range(q_heads):
             g = kv_head_of(h, q_heads, kv_heads)

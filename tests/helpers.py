@@ -41,7 +41,7 @@ def expected_step(sc, seqs=None, k_pool_bits=None, v_pool_bits=None):
     out = oracle.attention.decode(
         bits(sc.q), table_view(kp, sc.table_page_size), table_view(vp, sc.table_page_size),
         ints(sc.block_tables), ints(sc.context_lens), sc.table_page_size, sc.spec.window,
-        sc.scale, dt, seqs=seqs)
+        sc.scale, dt, seqs=seqs, sinks=getattr(sc.spec, "sinks", 0))
     return kp, vp, out
 
 

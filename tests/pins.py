@@ -271,5 +271,90 @@ def pin_copy():
     return P
 
 
+def _sink_rows_by_hand(L, W, S):
+    # the exercise's rule written out: every row while L <= W, else the first S
+    # rows and the last W - S
+    if L <= W:
+        return list(range(L))
+    return [i for i in range(L) if i < S or i >= L - (W - S)]
+
+
+def pin_sinks():
+    """Attention sinks (silicon-compiler chapter 15, "Exercises", exercise 3):
+    the exercise's case W = 6, S = 2; the context is W rows once L > W and every
+    row before; S = 0 is the plain window; the result equals brute force over
+    exactly the kept rows (rows in the hole hold data and must be ignored, and
+    unmapped hole pages must not be read); equal keys give the mean of exactly
+    those value rows; the sinks change the result."""
+    P = []
+    A = oracle.attention
+    if A.attended_rows(10, 6, 2) != [0, 1, 6, 7, 8, 9]:
+        P.append(f"W=6, S=2, L=10 must keep rows 0 1 6 7 8 9, got {A.attended_rows(10, 6, 2)}")
+    for W, S in ((6, 2), (5, 1), (9, 4), (3, 2)):
+        for L in range(0, 25):
+            got = A.attended_rows(L, W, S)
+            if got != _sink_rows_by_hand(L, W, S):
+                P.append(f"W={W} S={S} L={L}: rows {got}")
+            if len(got) != min(L, W):
+                P.append(f"W={W} S={S} L={L}: {len(got)} rows, the context must be min(L, W)")
+    for L in range(0, 15):
+        if A.attended_rows(L, 6, 0) != list(range(*A.live_rows(L, 6))):
+            P.append(f"S=0 must be the plain window at L={L}")
+    # full contexts stored (no window at build time), attended with sinks
+    spec = workloads.Spec(name="sinkfull", dtype="bf16", num_seqs=5, q_heads=4, kv_heads=2,
+                          head_dim=16, page_size=4, lens=(1, 5, 6, 7, 23), pool_factor=1.25)
+    sc = workloads.build(spec, 21, keep_source=True)
+    kp, vp, _ = expected_step(sc)
+    args = (bits(sc.q), kp, vp, ints(sc.block_tables), ints(sc.context_lens), 4)
+    qf = sc.q.to(torch.float64)
+    for W, S in ((6, 2), (3, 1), (10, 9)):
+        o = oracle.attention.decode(*args, W, sc.scale, "bf16", sinks=S)
+        win = oracle.attention.decode(*args, W, sc.scale, "bf16")
+        for s in range(5):
+            L = int(sc.lens[s])
+            rows = _sink_rows_by_hand(L, W, S)
+            k = sc.k_src[s].to(torch.float64)[rows].tolist()
+            v = sc.v_src[s].to(torch.float64)[rows].tolist()
+            ref = np.array(brute_attention(qf[s].tolist(), k, v, sc.scale, 4, 2))
+            if not np.max(np.abs(ref - o[s])) <= TOL:
+                P.append(f"W={W} S={S} seq {s}: differs from attention over rows {rows}")
+            if L > W and np.max(np.abs(o[s] - win[s])) < 1e-3:
+                P.append(f"W={W} S={S} seq {s}: the sinks made no difference")
+    # a pool built with sinks leaves the hole pages unmapped; the kept rows
+    # are the ones the generator wrote
+    spec = workloads.Spec(name="sinkholes", dtype="bf16", num_seqs=4, q_heads=4, kv_heads=2,
+                          head_dim=16, page_size=4, window=9, sinks=3, lens=(30, 9, 13, 4),
+                          pool_factor=1.25)
+    sc = workloads.build(spec, 23, keep_source=True)
+    kp, vp, _ = expected_step(sc)
+    o = oracle.attention.decode(bits(sc.q), kp, vp, ints(sc.block_tables), ints(sc.context_lens),
+                                4, 9, sc.scale, "bf16", sinks=3)
+    for s in range(4):
+        k, v = _src_lists(sc, s)
+        ref = np.array(brute_attention(sc.q.to(torch.float64)[s].tolist(), k, v,
+                                       sc.scale, 4, 2))
+        if not np.max(np.abs(ref - o[s])) <= TOL:
+            P.append(f"sink pool seq {s}: differs from brute force over the kept rows")
+    if int(ints(sc.block_tables)[0, 3]) != -1:
+        P.append("the sink pool must leave a hole in the table of a long sequence")
+    # equal keys: the mean of exactly the kept value rows
+    rng = np.random.default_rng(17)
+    Pg, Hkv, Hq, D = 4, 2, 4, 8
+    kf = rng.standard_normal((8, Pg, Hkv, D)).astype(np.float32)
+    vf = rng.standard_normal((8, Pg, Hkv, D)).astype(np.float32)
+    kf[...] = kf[0, 0][None, None]
+    table = np.array([[3, 6, 1, 0, 7, 2]])
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32).view(np.uint32)
+    o = oracle.attention.decode(q, kf.view(np.uint32), vf.view(np.uint32), table,
+                                np.array([22]), Pg, 7, 0.5, "f32", sinks=3)[0]
+    rows = [0, 1, 2, 18, 19, 20, 21]
+    mean = np.mean(np.stack([vf[table[0, i // Pg], i % Pg].astype(np.float64) for i in rows]), 0)
+    for h in range(Hq):
+        if np.max(np.abs(o[h] - mean[h // 2])) > 1e-13:
+            P.append("equal keys with sinks must give the mean of the kept value rows")
+            break
+    return P
+
+
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_window, pin_placement,
-            pin_slot_table, pin_store, pin_copy]
+            pin_slot_table, pin_store, pin_copy, pin_sinks]

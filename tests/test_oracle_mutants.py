@@ -13,6 +13,7 @@ from oracle import attention as A
 from oracle import kvstore as S
 
 _live, _gather, _head, _attend = A.live_rows, A.gather, A.kv_head_of, A.attend
+_rows, _gather_rows = A.attended_rows, A.gather_rows
 _store, _copy = S.store_kv, S.copy_pages
 
 
@@ -61,6 +62,21 @@ def _copy_keys_only(k, v, src, dst):
     return k2, v.copy()
 
 
+def _sinks_window_too_long(L, W, S=0):
+    # the window part keeps W rows instead of W - S
+    if W <= 0 or S <= 0:
+        return _rows(L, W, S)
+    return sorted(set(range(min(S, L))) | set(range(*_live(L, W))))
+
+
+def _gather_rows_first_dup(pool, table_row, rows, dtype):
+    # the first kept row read twice, the second never
+    rows = list(rows)
+    if len(rows) > 1:
+        rows[1] = rows[0]
+    return _gather_rows(pool, table_row, rows, dtype)
+
+
 MUTANTS = {
     "gather starts one row late": (A, "live_rows", lambda L, W: (min(_live(L, W)[0] + 1, L), L)),
     "window keeps W+1 rows": (A, "live_rows", lambda L, W: _live(L, W + 1 if W > 0 else 0)),
@@ -76,6 +92,10 @@ MUTANTS = {
     "store writes K into V": (S, "store_kv", _store_k_into_v),
     "copy-on-write copy is empty": (S, "copy_pages", _copy_empty),
     "copy forgets V": (S, "copy_pages", _copy_keys_only),
+    "sinks ignored": (A, "attended_rows", lambda L, W, S=0: _rows(L, W, 0)),
+    "sinks keep one row too many": (A, "attended_rows", lambda L, W, S=0: _rows(L, W, S + 1 if 0 < S < W - 1 else S)),
+    "window beside the sinks too long": (A, "attended_rows", _sinks_window_too_long),
+    "sink gather reads one row twice": (A, "gather_rows", _gather_rows_first_dup),
 }
 
 

@@ -52,6 +52,7 @@ class Spec:
     head_dim: int = 16
     page_size: int = 16
     window: int = 0                # 0: attend the whole context
+    sinks: int = 0                 # rows at the start kept besides the window (0 <= sinks < window)
     lens: Optional[tuple] = None   # explicit context lengths (include the new token)
     len_dist: str = "uniform"      # "uniform" | "lognormal" (when lens is None)
     len_lo: int = 1                # uniform: low bound; lognormal: median
@@ -187,6 +188,15 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
     if spec.prefix_len:
         assert W == 0 and spec.prefix_len % P == 0 and (lens > spec.prefix_len).all()
     lo = np.maximum(lens - W, 0) if W > 0 else np.zeros_like(lens)
+    S = spec.sinks
+    if S:
+        assert 0 < S < W and not spec.prefix_len and not spec.sibling_cow
+
+    def attended(L):
+        # the first S rows and the last W - S once the window cuts, else [lo, L)
+        if S and L > W:
+            return list(range(S)) + list(range(L - W + S, L))
+        return list(range(max(L - W, 0) if W > 0 else 0, L))
 
     # logical pages that must be mapped: those holding a row in [lo, L)
     first = lo // P
@@ -198,6 +208,12 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
         # the new row lands inside it exactly when (L-1) is not a page start
         cow = ((lens - 1) % P != 0) & ((lens - 1) // P >= n_shared)
     private = np.maximum(last - np.maximum(first, n_shared) + 1, 0)
+    page_sets = None
+    if S:
+        # with sinks the mapped pages are those of the attended rows (a hole between)
+        page_sets = [sorted({r // P for r in attended(int(L))}) for L in lens]
+        private = np.array([len(ps) for ps in page_sets], dtype=np.int64)
+        lo = np.array([int(L) - len(attended(int(L))) for L in lens], dtype=lens.dtype)
     needed = n_shared + int(private.sum()) + int(cow.sum())
     pool_pages = spec.pool_pages or int(math.ceil(spec.pool_factor * max(needed, 1)))
     assert pool_pages >= needed, "pool too small for the scenario"
@@ -207,6 +223,9 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
     shared = [next(take) for _ in range(n_shared)]
     seq_pages = []                     # per seq: dict logical page -> physical (pre-step)
     for s in range(B):
+        if page_sets is not None:
+            seq_pages.append({j: next(take) for j in page_sets[s]})
+            continue
         m = {j: shared[j] for j in range(first[s], min(last[s] + 1, n_shared))}
         for j in range(max(first[s], n_shared), last[s] + 1):
             m[j] = next(take)
@@ -257,6 +276,25 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
             if keep_source:
                 k_src.append(torch.zeros(0, Hkv, D, dtype=tdt))
                 v_src.append(torch.zeros(0, Hkv, D, dtype=tdt))
+            continue
+        if S:
+            # data only in the attended rows (sinks, then the window); the new row last
+            rows = attended(L)
+            kr = randn(len(rows), Hkv, D)
+            vr = randn(len(rows), Hkv, D)
+            if len(rows) > 1:
+                r = torch.tensor(rows[:-1])
+                pg = torch.tensor([seq_pages[s][int(j)] for j in (r // P).tolist()],
+                                  device=device, dtype=torch.long)
+                off = (r % P).to(device)
+                k_pool[pg, off] = kr[:-1]
+                v_pool[pg, off] = vr[:-1]
+            k_new[s] = kr[-1]
+            v_new[s] = vr[-1]
+            slots[s] = post_pages[s][(L - 1) // P] * P + (L - 1) % P
+            if keep_source:
+                k_src.append(kr.cpu())
+                v_src.append(vr.cpu())
             continue
         own0 = max(l0, spec.prefix_len)          # first private row that carries data
         kr = randn(L - own0, Hkv, D)
