@@ -13,6 +13,12 @@ Closed forms of the window rule (same chapter, section "The problem" and
   ``ceil(rows / P) - floor(keep_from / P)`` pages (0 if it holds no rows);
 * with a window of ``W`` tokens, after the trim that follows each step a
   request holds at most ``ceil((W - 1) / P) + 1`` pages.
+
+With ``S`` attention-sink rows kept besides a window of ``W - S`` (same
+chapter, section "Exercises", exercise 3) the first ``h = ceil(S / P)`` pages
+are never released, and the trim at ``L + 1 - (W - S)`` keeps at most
+``ceil((W - S - 1) / P) + 1`` pages after them, so a request holds at most
+``h + ceil((W - S - 1) / P) + 1`` pages.
 """
 from __future__ import annotations
 
@@ -59,3 +65,19 @@ def pages_exact(rows: int, keep_from: int, page: int) -> int:
 def window_bound(window: int, page: int) -> int:
     """Most pages a request holds after each step's trim, with a window."""
     return ceil_div(window - 1, page) + 1
+
+
+def pages_exact_sinks(rows: int, keep_from: int, head: int, page: int) -> int:
+    """Pages held when the first ``head`` pages are never released: every
+    page of the rows, less those after the head that end at or before
+    ``keep_from``."""
+    if rows <= 0:
+        return 0
+    total = ceil_div(rows, page)
+    released = min(max(keep_from // page - head, 0), max(total - head, 0))
+    return total - released
+
+
+def sink_bound(window: int, sinks: int, page: int) -> int:
+    """Most pages a request with ``sinks`` sink rows holds after each step's trim."""
+    return ceil_div(sinks, page) + ceil_div(window - sinks - 1, page) + 1

@@ -18,6 +18,10 @@ Semantics follow the page table of the silicon-compiler chapter 15 (section
   released one ends at or before ``keep_from``, so a page that still holds a
   needed row stays.  After a decode step at context ``L`` with window ``W``
   the next step needs rows ``>= L + 1 - W``.
+* with ``sinks`` rows kept at the start (the attention-sink exercise of that
+  chapter, section "Exercises"), the first ``ceil(sinks / P)`` pages are never
+  trimmed: the released pages then form a hole between them and the window,
+  and the table reads -1 there.
 * ``fork`` shares every page, a partial tail included, adding one reference
   each; ``release`` drops one reference to each page of the request.
 * a page whose count reaches zero goes back on the free list.
@@ -127,15 +131,19 @@ class PagedKVCache:
         self.pool = BlockAllocator(num_pages, policy, free_order)
         self.pages: Dict[Hashable, List[int]] = {}    # live pages, oldest first
         self.length: Dict[Hashable, int] = {}
-        self.dropped: Dict[Hashable, int] = {}        # front pages released by trim
+        self.dropped: Dict[Hashable, int] = {}        # pages released by trim
+        self.head: Dict[Hashable, int] = {}           # leading pages kept for sink rows
 
     # -- lifecycle -------------------------------------------------------------
-    def new(self, rid: Hashable) -> None:
+    def new(self, rid: Hashable, sinks: int = 0) -> None:
         if rid in self.pages:
             raise KeyError(f"request {rid!r} exists")
+        if sinks < 0:
+            raise ValueError("sinks must be >= 0")
         self.pages[rid] = []
         self.length[rid] = 0
         self.dropped[rid] = 0
+        self.head[rid] = -(-sinks // self.page_size)
 
     def append(self, rid: Hashable) -> AppendPlan:
         """Place one new row at the end of request ``rid``."""
@@ -160,12 +168,14 @@ class PagedKVCache:
         return AppendPlan(rid, row, page, off, page * P + off, plan_copy, new_page)
 
     def trim(self, rid: Hashable, keep_from: int) -> List[int]:
-        """Release front pages lying wholly before row ``keep_from``; returns them."""
+        """Release pages lying wholly before row ``keep_from``, sink pages
+        excepted; returns them."""
         P = self.page_size
         pages = self.pages[rid]
+        h = self.head[rid]
         out = []
-        while pages and (self.dropped[rid] + 1) * P <= keep_from:
-            p = pages.pop(0)
+        while len(pages) > h and (h + self.dropped[rid] + 1) * P <= keep_from:
+            p = pages.pop(h)
             self.pool.unref(p)
             self.dropped[rid] += 1
             out.append(p)
@@ -177,6 +187,7 @@ class PagedKVCache:
         self.pages[dst] = list(self.pages[src])
         self.length[dst] = self.length[src]
         self.dropped[dst] = self.dropped[src]
+        self.head[dst] = self.head[src]
         for p in self.pages[dst]:
             self.pool.incref(p)
 
@@ -185,6 +196,7 @@ class PagedKVCache:
             self.pool.unref(p)
         del self.length[rid]
         del self.dropped[rid]
+        del self.head[rid]
 
     def rewind(self, rid: Hashable, n: int) -> List[int]:
         """Drop the newest ``n`` rows; pages left without a row are released."""
@@ -192,9 +204,10 @@ class PagedKVCache:
             raise ValueError("cannot rewind past the start")
         P = self.page_size
         new_len = self.length[rid] - n
-        keep = -(-new_len // P) - self.dropped[rid]
-        if keep < 0:
+        d, h = self.dropped[rid], self.head[rid]
+        if d > 0 and new_len < (h + d) * P:
             raise ValueError("cannot rewind into released pages")
+        keep = -(-new_len // P) - d
         pages = self.pages[rid]
         out = []
         while len(pages) > keep:
@@ -211,13 +224,19 @@ class PagedKVCache:
     def translate(self, rid: Hashable, row: int) -> Tuple[int, int]:
         """(physical page, offset) of a readable logical row."""
         P = self.page_size
-        if not self.dropped[rid] * P <= row < self.length[rid]:
+        j, h, d = row // P, self.head[rid], self.dropped[rid]
+        if not 0 <= row < self.length[rid] or h <= j < h + d:
             raise IndexError(f"row {row} of request {rid!r} is not readable")
-        return self.pages[rid][row // P - self.dropped[rid]], row % P
+        return self.pages[rid][j if j < h else j - d], row % P
+
+    def logical_page(self, rid: Hashable, i: int) -> int:
+        """Logical page index of the ``i``-th live page of a request."""
+        return i if i < self.head[rid] else i + self.dropped[rid]
 
     def table(self, rid: Hashable) -> List[int]:
         """Block table indexed by logical page; -1 for released pages."""
-        return [-1] * self.dropped[rid] + list(self.pages[rid])
+        h, pages = self.head[rid], self.pages[rid]
+        return list(pages[:h]) + [-1] * self.dropped[rid] + list(pages[h:])
 
     @staticmethod
     def pages_needed(cached_len: int, device_len: int, page_size: int) -> int:
@@ -248,9 +267,8 @@ class PagedKVCache:
             L = self.length[rid]
             if L > stride:
                 raise ValueError(f"request {rid!r} has {L} rows > {stride}")
-            d = self.dropped[rid]
             for j, p in enumerate(self.pages[rid]):
-                r0 = (d + j) * P
+                r0 = self.logical_page(rid, j) * P
                 r1 = min(r0 + P, L)
                 out[i, r0:r1] = p * P + np.arange(r1 - r0)
         if out.max(initial=0) >= 2**31:
