@@ -15,7 +15,8 @@
  *   pa_decode      single-query attention of every sequence over its rows,
  *                  reached through a per-sequence block table, optionally
  *                  limited to the last W rows (silicon chapter 15, sections
- *                  "The problem" and "The model"; the dense result it must
+ *                  "The problem" and "The model"; pa_decode_sinks also keeps
+ *                  the first rows, "Exercises"; the dense result it must
  *                  equal is the checkpoint of the tiny-llm page "Paged KV
  *                  Cache", section "Correctness Checkpoint").
  *
@@ -128,6 +129,28 @@ int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
               int32_t num_pages, int32_t page_size, int32_t window, int32_t max_context_len,
               float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
               void* stream);
+
+/*
+ * pa_decode_sinks -- pa_decode with attention sinks (silicon chapter 15,
+ * section "Exercises", the attention-sink exercise): besides the window, the
+ * first `sinks` rows of every sequence stay attended.
+ *   sinks         0 <= sinks < window when window > 0; 0 when window <= 0.
+ *                 Once L > window the attended rows are [0, sinks) and
+ *                 [L - window + sinks, L) -- still `window` rows; while
+ *                 L <= window every row [0, L).  sinks = 0 is pa_decode.
+ *                 The block table may read -1 for the pages between the two
+ *                 runs (a page holding a sink row or a window row must be
+ *                 mapped; rows between them are never read or weighted).
+ *   Every other argument, the workspace rules and the supported shapes are
+ *   those of pa_decode (a workspace sized for sinks may be larger).
+ *   Errors: PA_EINVAL for sinks < 0, or sinks > 0 without a window above it.
+ */
+int pa_decode_sinks(float* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                    int32_t kv_heads, int32_t head_dim, int32_t num_pages, int32_t page_size,
+                    int32_t window, int32_t sinks, int32_t max_context_len, float scale,
+                    int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,9 @@ SIGNATURES = {
     "pa_copy_pages": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                  ctypes.c_float, _I, _P, ctypes.POINTER(ctypes.c_size_t), _P]),
+    "pa_decode_sinks": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       _I, _I, ctypes.c_float, _I, _P,
+                                       ctypes.POINTER(ctypes.c_size_t), _P]),
 }
 
 _lib = None

@@ -16,6 +16,7 @@ struct DecodeArgs {
   int bt_stride;
   int num_seqs, q_heads, kv_heads, group;
   int num_pages, page_size, window;
+  int sinks;                   // rows at the start kept besides the window (0 <= sinks < window)
   int max_ctx;                 // host bound on context lengths; longer ones are clamped to it
   int max_chunks, chunk;       // rows per chunk; chunks per sequence at most
   float qscale;                // scale * log2(e): logits are kept in base 2
@@ -34,6 +35,34 @@ __device__ __forceinline__ void live_range(int ctx, int window, int max_ctx, int
   L = ctx > 0 ? (ctx < max_ctx ? ctx : max_ctx) : 0;
   lo = (window > 0 && L > window) ? L - window : 0;
   n = L - lo;
+}
+
+// The same with attention sinks (the sink exercise of "A Paged KV Cache and Sliding-Window
+// Attention", section "Exercises"): once L exceeds the window W, the first S rows and the
+// last W - S, i.e. rows [0, sl) and [lo, L) with sl = S and lo = L - W + S; before that
+// every row, sl = 0 and lo = 0.  With S = 0 this is live_range.
+__device__ __forceinline__ void sink_ranges(int ctx, int window, int sinks, int max_ctx, int& L,
+                                            int& sl, int& lo) {
+  L = ctx > 0 ? (ctx < max_ctx ? ctx : max_ctx) : 0;
+  const bool cut = window > 0 && L > window;
+  sl = cut ? sinks : 0;
+  lo = cut ? L - window + sinks : 0;
+}
+
+// Chunks of `chunk` rows over the two runs: first over [0, sl), then over [lo, L).
+__device__ __forceinline__ int chunk_count(int L, int sl, int lo, int chunk) {
+  return (sl + chunk - 1) / chunk + (L - lo + chunk - 1) / chunk;
+}
+__device__ __forceinline__ void chunk_span(int c, int L, int sl, int lo, int chunk, int& tb,
+                                           int& te) {
+  const int ns = (sl + chunk - 1) / chunk;
+  if (c < ns) {
+    tb = c * chunk;
+    te = min(sl, tb + chunk);
+  } else {
+    tb = lo + (c - ns) * chunk;
+    te = min(L, tb + chunk);
+  }
 }
 
 }  // namespace pa

@@ -93,9 +93,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int s = rest / a.max_chunks;
   const int G = a.group;
 
-  int L, lo, n;
-  live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
-  const int nch = (n + a.chunk - 1) / a.chunk;
+  int L, sl, lo;
+  sink_ranges(a.ctx[s], a.window, a.sinks, a.max_ctx, L, sl, lo);
+  const int nch = chunk_count(L, sl, lo, a.chunk);
   float* out_base = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
   if (nch == 0) {
     if (c == 0)
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 
   const int P = a.page_size;
   const int lp = 31 - __clz(P);  // page size is a power of two on this path
-  const int t_begin = lo + c * a.chunk;
-  const int t_end = min(L, t_begin + a.chunk);
+  int t_begin, t_end;
+  chunk_span(c, L, sl, lo, a.chunk, t_begin, t_end);
   const int j0 = t_begin >> lp;
   const int nj = ((t_end - 1) >> lp) - j0 + 1;
   const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;

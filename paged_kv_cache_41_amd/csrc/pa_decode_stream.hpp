@@ -85,8 +85,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 struct Cur {
   int s, g, k;      // sequence, kv head, tile within the segment
   int tiles;        // tiles of the segment
-  int lo, L;        // attended rows [lo, L)
-  int t0base;       // first row of tile 0: lo rounded down to a multiple of 16
+  int sl, lo, L;    // attended rows [0, sl) and [lo, L)
+  int sk;           // tiles of the sink rows: tiles 0 .. sk-1 start at rows 0, 16, ...
+  int t0base;       // added to 16 k for the later tiles: the window's tiles start at row
+                    // 16 max(sk, lo / 16)
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -144,7 +146,7 @@ enum : int {
 struct Desc {
   int s, g;          // sequence, kv head
   int t0;            // first row of the tile
-  int lo, L;         // attended rows [lo, L) of the sequence
+  int sl, lo, L;     // attended rows [0, sl) and [lo, L) of the sequence
   int flags;
 };
 
@@ -160,13 +162,16 @@ struct Front {
   int rem;            // tiles of the range from the front on (1: the front is on its last)
   bool first;         // the front is on the first tile of the range
   bool idle;
-  int B, Hkv, window;
+  int B, Hkv, window, sinks;
 
   __device__ __forceinline__ void seg_fields() {
     f.tiles = uni(st_cum[f.s + 1] - st_cum[f.s]);
     f.L = uni(st_len[f.s]);
-    f.lo = (window > 0 && f.L > window) ? f.L - window : 0;
-    f.t0base = (f.lo >> 4) << 4;
+    const bool cut = window > 0 && f.L > window;
+    f.sl = cut ? sinks : 0;
+    f.lo = cut ? f.L - window + sinks : 0;
+    f.sk = (f.sl + 15) >> 4;
+    f.t0base = (max(f.sk, f.lo >> 4) - f.sk) << 4;
   }
   // position of flattened tile x
   __device__ __forceinline__ void locate(int x) {
@@ -201,7 +206,8 @@ struct Front {
     Desc d;
     d.s = f.s;
     d.g = f.g;
-    d.t0 = f.t0base + f.k * TILE;
+    d.t0 = f.k * TILE + (f.k >= f.sk ? f.t0base : 0);
+    d.sl = f.sl;
     d.lo = f.lo;
     d.L = f.L;
     d.flags = idle ? IDLE
@@ -237,9 +243,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     for (int i = 0; i < per; ++i) {
       const int s = tid * per + i;
       if (s < B) {
-        int L, lo, n;
-        live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
-        const int t = n > 0 ? ((L - 1) >> 4) - (lo >> 4) + 1 : 0;
+        int L, sl, lo;
+        sink_ranges(a.ctx[s], a.window, a.sinks, a.max_ctx, L, sl, lo);
+        // sink tiles, then the window's tiles from the first one past them
+        const int sk = (sl + 15) >> 4;
+        const int t = L > 0 ? sk + ((L - 1) >> 4) - max(sk, lo >> 4) + 1 : 0;
         st_len[s] = L;
         st_cum[s] = t;
         local += t;
@@ -297,6 +305,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   fr.B = B;
   fr.Hkv = Hkv;
   fr.window = a.window;
+  fr.sinks = a.sinks;
   fr.locate(ta);
   fr.rem = n;
   fr.first = true;
@@ -305,16 +314,18 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // Table entries.  With pages of at least 16 rows the tile lies in one page: one entry,
   // read through the scalar path (constant address space), whose completion is counted
   // apart from the vector loads, so waiting for it never drains the K/V tiles in flight.
-  // Smaller pages need one entry per token (lane col holds token t0 + col's).
+  // Smaller pages need one entry per token (lane col holds token t0 + col's).  Rows outside
+  // the attended ones are clamped to one that is, so their entries are mapped pages.
   const __attribute__((address_space(4))) int32_t* bt_const =
       (const __attribute__((address_space(4))) int32_t*)a.block_tables;
   auto table_entry = [&](const Desc& d) {
     if constexpr (PAGE_TILES) {
-      const int t = min(max(d.t0, d.lo), d.L - 1);
+      const int t = d.t0 < d.sl ? d.t0 : min(max(d.t0, d.lo), d.L - 1);
       // num_seqs * bt_stride < 2^31 on this path, so the index fits one scalar register
       return bt_const[uni(d.s * a.bt_stride + (t >> lp))];
     } else {
-      const int t = min(max(d.t0 + col, d.lo), d.L - 1);
+      const int tc = d.t0 + col;
+      const int t = tc < d.sl ? tc : min(max(tc, d.lo), d.L - 1);
       return a.block_tables[(size_t)d.s * a.bt_stride + (t >> lp)];
     }
   };
@@ -345,8 +356,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       // one page for the whole tile: a uniform base address plus constant lane offsets
       const int pg = uni(e);
       const bool mapped = pg >= 0 && pg <= last_page;
-      const int lo_off = max(d.lo - t0, 0), hi_off = min(d.L - t0, TILE);
-      const uint32_t bits = ((1u << hi_off) - 1u) & ~((1u << lo_off) - 1u);
+      const int lo_off = min(max(d.lo - t0, 0), TILE), hi_off = min(d.L - t0, TILE);
+      const int sl_off = min(max(d.sl - t0, 0), TILE);
+      const uint32_t bits = ((1u << hi_off) - 1u) & (~((1u << lo_off) - 1u) | ((1u << sl_off) - 1u));
       Tl.valid = mapped ? (uint64_t)bits : 0ull;
       const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
                             (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)d.g * HD * 2;
@@ -359,16 +371,18 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       return;
     }
     const int tk = t0 + col;
-    Tl.valid = __ballot(tk >= d.lo && tk < d.L && e >= 0 && e <= last_page) & 0xffffull;
+    Tl.valid = __ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e >= 0 && e <= last_page) &
+               0xffffull;
     const uint32_t hoff = (uint32_t)d.g * HD * 2;
-    const int tkc = min(max(tk, d.lo), d.L - 1);
+    const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
     const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 64);
 #pragma unroll
     for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ev = __shfl(e, 4 * grp + j, 64);
-      const int tv = min(max(t0 + 4 * grp + j, d.lo), d.L - 1);
+      const int tr = t0 + 4 * grp + j;
+      const int tv = tr < d.sl ? tr : min(max(tr, d.lo), d.L - 1);
       Tl.v[j] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
     }
   };
@@ -639,16 +653,20 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 }
 
 // Tiles of the list at most: every segment covers ceil(n / 16) + 1 tiles at most.
-inline int64_t tiles_bound(int num_seqs, int kv_heads, int max_live) {
-  return (int64_t)num_seqs * kv_heads * ((max_live + 15) / 16 + 1);
+// Tiles of the whole list at most: max_live attended rows per sequence, of which `sinks`
+// may form a run of their own at the start.
+inline int64_t tiles_bound(int num_seqs, int kv_heads, int max_live, int sinks) {
+  const int per = sinks > 0 ? (sinks + 15) / 16 + (max_live - sinks + 15) / 16 + 1
+                            : (max_live + 15) / 16 + 1;
+  return (int64_t)num_seqs * kv_heads * per;
 }
 
 inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs,
-                     int bt_stride, int kv_heads, int max_live) {
+                     int bt_stride, int kv_heads, int max_live, int sinks) {
   return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 && page_size > 0 &&
          (page_size & (page_size - 1)) == 0 && num_seqs >= 1 && num_seqs <= BMAX &&
          (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31) &&
-         tiles_bound(num_seqs, kv_heads, max_live) < ((int64_t)1 << 30);
+         tiles_bound(num_seqs, kv_heads, max_live, sinks) < ((int64_t)1 << 30);
 }
 
 // Workspace: the arrival counters (zero between calls), then per wavefront two partial

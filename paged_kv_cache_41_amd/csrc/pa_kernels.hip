@@ -118,9 +118,9 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   const int sub = lane % LPT;
   const int tok = lane / LPT;
 
-  int L, lo, n;
-  live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
-  const int nch = (n + a.chunk - 1) / a.chunk;
+  int L, sl, lo;
+  sink_ranges(a.ctx[s], a.window, a.sinks, a.max_ctx, L, sl, lo);
+  const int nch = chunk_count(L, sl, lo, a.chunk);
   float* outp = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * D + sub * EPL;
   if (nch == 0) {
     if (c == 0 && tok == 0)
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   const T* vp = reinterpret_cast<const T*>(a.v_pool);
   const size_t row_stride = (size_t)Hkv * D;
   const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
-  const int t_begin = lo + c * a.chunk;
-  const int t_end = min(L, t_begin + a.chunk);
+  int t_begin, t_end;
+  chunk_span(c, L, sl, lo, a.chunk, t_begin, t_end);
 
   for (int t0 = t_begin; t0 < t_end; t0 += TPW) {
     const int t = t0 + tok;
@@ -239,9 +239,9 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int D) {
   const int h = blockIdx.x % a.q_heads;
   const int s = blockIdx.x / a.q_heads;
-  int L, lo, n;
-  live_range(a.ctx[s], a.window, a.max_ctx, L, lo, n);
-  const int nch = (n + a.chunk - 1) / a.chunk;
+  int L, sl, lo;
+  sink_ranges(a.ctx[s], a.window, a.sinks, a.max_ctx, L, sl, lo);
+  const int nch = chunk_count(L, sl, lo, a.chunk);
   if (nch <= 1) return;
   const size_t base = ((size_t)s * a.q_heads + h) * a.max_chunks;
   const float* ml = a.ws_ml + 2 * base;
@@ -373,13 +373,16 @@ extern "C" int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_page
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
-extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* block_tables, int32_t bt_stride,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
-                         int32_t kv_heads, int32_t head_dim, int32_t num_pages,
-                         int32_t page_size, int32_t window, int32_t max_context_len, float scale,
-                         int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream) {
+extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t num_pages, int32_t page_size, int32_t window,
+                               int32_t sinks, int32_t max_context_len, float scale,
+                               int32_t dtype, void* workspace, size_t* workspace_bytes,
+                               void* stream) {
   if (!workspace_bytes) return PA_EINVAL;
+  if (sinks < 0 || (sinks > 0 && (window <= 0 || sinks >= window))) return PA_EINVAL;
   if (num_seqs < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || num_pages <= 0 ||
       page_size <= 0 || bt_stride <= 0)
     return PA_EINVAL;
@@ -397,11 +400,14 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
   if (!generic) return PA_EUNSUPPORTED;
 
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
+  // sink rows form a run of their own only where the window can cut a context
+  const int run_sinks = window > 0 && window < max_context_len ? sinks : 0;
   DecodeArgs a{};
+  a.sinks = window > 0 ? sinks : 0;
   if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
-                       max_live)) {
+                       max_live, run_sinks)) {
     // balanced streaming path: wavefronts and chunks sized to the largest possible list
-    const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live);
+    const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live, run_sinks);
     // about 22 tiles per wavefront at least (so the start-up and the end of a range stay
     // small next to its stream), at most stream_waves_max
     int64_t waves = tiles_max / 22;
@@ -442,7 +448,9 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
   a.chunk = pick_chunk(max_live);
   const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
   if (fast) a.chunk = mfma::chunk_for(num_seqs, kv_heads, max_live);
-  a.max_chunks = (max_live + a.chunk - 1) / a.chunk;
+  a.max_chunks = run_sinks > 0 ? (run_sinks + a.chunk - 1) / a.chunk +
+                                     (max_live - run_sinks + a.chunk - 1) / a.chunk
+                                : (max_live + a.chunk - 1) / a.chunk;
   if (a.max_chunks < 1) a.max_chunks = 1;
   const size_t parts = (size_t)num_seqs * q_heads * a.max_chunks;
   const size_t need = parts * ((size_t)head_dim + 2) * sizeof(float);
@@ -489,4 +497,15 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
     if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
   }
   return PA_OK;
+}
+
+extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t bt_stride,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                         int32_t kv_heads, int32_t head_dim, int32_t num_pages,
+                         int32_t page_size, int32_t window, int32_t max_context_len, float scale,
+                         int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream) {
+  return pa_decode_sinks(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens,
+                         num_seqs, q_heads, kv_heads, head_dim, num_pages, page_size, window, 0,
+                         max_context_len, scale, dtype, workspace, workspace_bytes, stream);
 }

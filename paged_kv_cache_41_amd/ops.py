@@ -81,36 +81,41 @@ def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
         int(src_pages.numel()), n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
 
 
-def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, scale,
+def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, ws_ptr, ws_size, stream_handle):
     n, P, hkv, d = _pool_dims(k_pool, v_pool)
     B, hq, dq = (int(x) for x in q.shape)
     lib = _lib.load()
     size = ctypes.c_size_t(ws_size)
-    st = lib.pa_decode(
-        out.data_ptr() if out is not None else None, q.data_ptr(), k_pool.data_ptr(),
-        v_pool.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
-        context_lens.data_ptr(), B, hq, hkv, d, n, P, int(window), int(max_context_len),
-        float(scale), _code(q), ws_ptr, ctypes.byref(size), stream_handle)
-    _lib.check("pa_decode", st)
+    head = (out.data_ptr() if out is not None else None, q.data_ptr(), k_pool.data_ptr(),
+            v_pool.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
+            context_lens.data_ptr(), B, hq, hkv, d, n, P, int(window))
+    tail = (int(max_context_len), float(scale), _code(q), ws_ptr, ctypes.byref(size),
+            stream_handle)
+    if sinks:
+        _lib.check("pa_decode_sinks", lib.pa_decode_sinks(*head, int(sinks), *tail))
+    else:
+        _lib.check("pa_decode", lib.pa_decode(*head, *tail))
     return size.value
 
 
 def decode_workspace_bytes(q, k_pool, v_pool, block_tables, context_lens, *, window=0,
-                           max_context_len=0) -> int:
+                           sinks=0, max_context_len=0) -> int:
     """Bytes of device workspace ``decode`` needs for these operands."""
-    return _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, 1.0,
-                        max_context_len, None, 0, None)
+    return _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, sinks,
+                        1.0, max_context_len, None, 0, None)
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
-           scale: Optional[float] = None, max_context_len: int = 0,
+           sinks: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
     """Single-query paged attention; returns fp32 ``[num_seqs, q_heads, head_dim]``.
 
     A raw token-slot table is passed as ``block_tables`` together with pools
     viewed in pages of one row (``pool.view(-1, 1, kv_heads, head_dim)``).
+    ``sinks > 0`` (below ``window``) also attends the first ``sinks`` rows of
+    every sequence, through ``pa_decode_sinks``; 0 calls ``pa_decode``.
     A ``workspace`` passed in must be zero-filled before its first use; each call
     leaves it ready for the next.  Without one (or with one too small) a zeroed
     workspace is allocated for this call.
@@ -130,11 +135,11 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
         out = torch.empty(B, q.shape[1], d, dtype=torch.float32, device=dev)
     elif out.shape != (B, q.shape[1], d) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 [num_seqs, q_heads, head_dim]")
-    need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, scale,
-                        max_context_len, None, 0, None)
+    need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, sinks,
+                        scale, max_context_len, None, 0, None)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
-    _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, scale,
+    _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, workspace.data_ptr(),
                  workspace.numel() * workspace.element_size(), _stream(dev, stream))
     return out

@@ -63,6 +63,17 @@ def test_argument_validation_needs_no_gpu():
     # max_context_len beyond what the table can address
     assert lib.pa_decode(None, None, None, None, None, 4, None, 1, 4, 4, 128, 8, 16, 0, 65, 1.0,
                          1, None, ctypes.byref(size), None) == _lib.PA_EINVAL
+    # sinks: negative, without a window, not below the window; a valid query
+    sink = lambda window, sinks: lib.pa_decode_sinks(
+        None, None, None, None, None, 256, None, 64, 32, 8, 128, 1000, 16, window, sinks, 4096,
+        1.0, 1, None, ctypes.byref(size), None)
+    assert sink(0, -1) == _lib.PA_EINVAL
+    assert sink(0, 4) == _lib.PA_EINVAL
+    assert sink(64, 64) == _lib.PA_EINVAL and sink(64, 100) == _lib.PA_EINVAL
+    size.value = 0
+    assert sink(1024, 4) == _lib.PA_OK and size.value > 0
+    with_sinks = size.value
+    assert sink(1024, 0) == _lib.PA_OK and size.value <= with_sinks
     # store / copy: bad dtype, zero-sized no-ops
     assert lib.pa_store_kv(None, None, None, None, None, 1, 8, 16, 8, 128, 7, None) == _lib.PA_EINVAL
     assert lib.pa_store_kv(None, None, None, None, None, 0, 8, 16, 8, 128, 1, None) == _lib.PA_OK

@@ -44,7 +44,7 @@ def gpu_step(sc):
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
     kv, vv = decode_views(sc)
     out = o.decode(sc.q, kv, vv, sc.block_tables, sc.context_lens, window=sc.spec.window,
-                   scale=sc.scale, max_context_len=sc.max_context_len)
+                   sinks=sc.spec.sinks, scale=sc.scale, max_context_len=sc.max_context_len)
     torch.cuda.synchronize()
     return kp0, vp0, out
 
@@ -100,6 +100,76 @@ def test_batch_above_streaming_limit(window):
     seqs = sorted(set(rng.choice(2100, 40, replace=False).tolist()) |
                   {0, 2099, int(np.argmax(sc.lens)), int(np.argmin(sc.lens))})
     check_step(sc, seqs=seqs)
+
+
+# Attention sinks: the first S rows plus the last W - S.  The pools map only the pages of
+# those rows (the table reads -1 between them), and rows of mapped pages that are not
+# attended hold canaries or NaN, so a row read or weighted by mistake shows.
+_GQA = dict(dtype="bf16", q_heads=32, kv_heads=8, head_dim=128)
+SINKS = {
+    "stream_p16_s4": dict(_GQA, num_seqs=64, page_size=16, window=256, sinks=4, len_lo=1,
+                          len_hi=1200),
+    "stream_p16_s40_nan": dict(_GQA, num_seqs=48, page_size=16, window=100, sinks=40,
+                               len_lo=1, len_hi=700, spare="nan"),
+    "stream_p16_s16": dict(_GQA, num_seqs=40, page_size=16, window=48, sinks=16, len_lo=1,
+                           len_hi=300),
+    "stream_p4_s10_w12": dict(_GQA, num_seqs=40, page_size=4, window=12, sinks=10, len_lo=1,
+                              len_hi=90, spare="nan"),
+    "stream_p8_s3": dict(_GQA, num_seqs=30, page_size=8, window=77, sinks=3, len_lo=1,
+                         len_hi=400),
+    "stream_slots_s5": dict(_GQA, num_seqs=24, page_size=16, window=64, sinks=5, len_lo=1,
+                            len_hi=500, slot_table=True),
+    "stream_g1_s2": dict(dtype="bf16", q_heads=8, kv_heads=8, head_dim=128, num_seqs=16,
+                         page_size=32, window=40, sinks=2, len_lo=1, len_hi=200),
+    "f32_generic_s3": dict(dtype="f32", q_heads=8, kv_heads=2, head_dim=64, num_seqs=20,
+                           page_size=4, window=30, sinks=3, len_lo=1, len_hi=150, spare="nan"),
+    "bf16_d32_s7": dict(dtype="bf16", q_heads=4, kv_heads=1, head_dim=32, num_seqs=20,
+                        page_size=2, window=20, sinks=7, len_lo=1, len_hi=100),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SINKS))
+def test_sinks(name):
+    sc = workloads.build(workloads.Spec(name=f"sinks_{name}", pool_factor=1.25, **SINKS[name]),
+                         31, device="cuda")
+    assert (sc.lens > sc.spec.window).any() and (sc.lens <= sc.spec.window).any()
+    check_step(sc)
+
+
+def test_sinks_batch_above_streaming_limit():
+    # the chunked matrix-core path: sink chunks, then window chunks
+    spec = workloads.Spec(name="sinks_b2100", dtype="bf16", num_seqs=2100, q_heads=16,
+                          kv_heads=4, head_dim=128, page_size=16, window=200, sinks=24,
+                          len_lo=1, len_hi=700, pool_factor=1.25, spare="nan")
+    sc = workloads.build(spec, 17, device="cuda")
+    rng = np.random.default_rng(3)
+    seqs = sorted(set(rng.choice(2100, 40, replace=False).tolist()) |
+                  {0, 2099, int(np.argmax(sc.lens)), int(np.argmin(sc.lens))})
+    check_step(sc, seqs=seqs)
+
+
+def test_sinks_equal_window_rows_differ_from_plain_window():
+    # same pool, all rows stored: sinks change the result exactly where L > W
+    spec = workloads.Spec(name="sinks_vs_window", **_GQA, num_seqs=32, page_size=16,
+                          len_lo=1, len_hi=600, pool_factor=1.25)
+    sc = workloads.build(spec, 5, device="cuda")
+    o = ops()
+    o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    args = (sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens)
+    W, S = 160, 8
+    a = o.decode(*args, window=W, scale=sc.scale).cpu().double().numpy()
+    b = o.decode(*args, window=W, sinks=S, scale=sc.scale).cpu().double().numpy()
+    kp, vp = bits(sc.k_pool), bits(sc.v_pool)
+    ref = oracle.attention.decode(bits(sc.q), kp, vp, ints(sc.block_tables), ints(sc.context_lens),
+                                  16, W, sc.scale, "bf16", sinks=S)
+    assert float(np.max(np.abs(b - ref))) <= TOL["bf16"]
+    cut = sc.lens > W
+    assert cut.any() and (~cut).any()
+    # uncut sequences attend the same rows; the partition of the batch into ranges differs
+    # between the two calls (more tiles with sinks), so only the rounding order may differ
+    assert float(np.max(np.abs(a[~cut] - b[~cut]))) <= 1e-5
+    assert (np.max(np.abs(a[cut] - b[cut]), axis=(1, 2)) > 1e-3).all()
 
 
 @pytest.mark.parametrize("seed", range(40))

@@ -123,7 +123,7 @@ class Scenario:
     seed: int
     device: str
     lens: np.ndarray                 # int64 [B], context length incl. the new token
-    lo: np.ndarray                   # int64 [B], first attended row
+    lo: np.ndarray                   # int64 [B], L less the rows attended (with no sinks: the first attended row)
     pool_pages: int                  # physical pages, incl. the dummy page in slot mode
     k_pool: torch.Tensor             # [pool_pages, page_size, kv_heads, head_dim]
     v_pool: torch.Tensor
@@ -138,7 +138,8 @@ class Scenario:
     copy_dst: torch.Tensor
     scale: float
     max_context_len: int
-    # the unpaged rows [lo, L) of every sequence (last one = the new row), CPU, if kept
+    # the unpaged attended rows of every sequence in row order (last one = the new row), CPU,
+    # if kept
     k_src: Optional[List[torch.Tensor]] = None
     v_src: Optional[List[torch.Tensor]] = None
     shared_pages: int = 0            # pages of the shared prefix (mapped by every sequence)
