@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--sinks", type=int, default=0,
+                   help="attention-sink rows kept besides the window (workloads with a window)")
     p.add_argument("--warm-steps", type=int, default=None,
                    help="also time this many back-to-back steps without a flush "
                         "(default: --steps; 0: skip)")
@@ -67,9 +69,19 @@ def decode_bytes(sc) -> dict:
     n = sc.lens - sc.lo
     kv = int((2 * n * s.kv_heads * s.head_dim * elt).sum())
     tps = sc.table_page_size
-    first = sc.lo // tps
-    last = np.where(sc.lens > 0, (sc.lens - 1) // tps, first - 1)
-    table = int((4 * (last - first + 1)).clip(min=0).sum())
+    if s.sinks:
+        # table entries of the sink rows' pages and of the window's (the hole is skipped)
+        W, S = s.window, s.sinks
+        table = 0
+        for L in sc.lens.tolist():
+            if L > W:
+                table += 4 * (-(-S // tps) + (L - 1) // tps - max(-(-S // tps), (L - W + S) // tps) + 1)
+            elif L > 0:
+                table += 4 * ((L - 1) // tps + 1)
+    else:
+        first = sc.lo // tps
+        last = np.where(sc.lens > 0, (sc.lens - 1) // tps, first - 1)
+        table = int((4 * (last - first + 1)).clip(min=0).sum())
     q = s.num_seqs * s.q_heads * s.head_dim * elt
     out = s.num_seqs * s.q_heads * s.head_dim * 4
     return {"kv": kv, "total": kv + table + q + out + 4 * s.num_seqs,
@@ -172,7 +184,8 @@ def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
     with threadpool_limits(limits=1):
         while time.perf_counter() - t0 < budget_s:
             i = done % s.num_seqs
-            oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype, seqs=[i])
+            oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype, seqs=[i],
+                                    sinks=s.sinks)
             kv_bytes += int(2 * (sc.lens[i] - sc.lo[i]) * s.kv_heads * s.head_dim * elt)
             done += 1
     dt = time.perf_counter() - t0
@@ -199,14 +212,22 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    sc = workloads.make_config(args.config, seed=args.seed, device="cuda:0")
+    over = {}
+    if args.sinks:
+        base = workloads.config_spec(args.config)
+        if base.window <= args.sinks:
+            print(f"--sinks {args.sinks} needs a workload whose window is wider "
+                  f"(workload {args.config} has window {base.window})", file=sys.stderr)
+            sys.exit(2)
+        over = dict(sinks=args.sinks, name=f"{base.name}_sinks{args.sinks}")
+    sc = workloads.make_config(args.config, seed=args.seed, device="cuda:0", **over)
     s = sc.spec
     hkv, d = s.kv_heads, s.head_dim
     kv_view = (sc.k_pool, sc.v_pool) if sc.table_page_size == s.page_size else (
         sc.k_pool.view(-1, 1, hkv, d), sc.v_pool.view(-1, 1, hkv, d))
     out = torch.empty(s.num_seqs, s.q_heads, d, dtype=torch.float32, device=dev)
     need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
-                                      sc.context_lens, window=s.window,
+                                      sc.context_lens, window=s.window, sinks=s.sinks,
                                       max_context_len=sc.max_context_len)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     flush = None
@@ -228,7 +249,8 @@ def main():
 
     def attend():
         ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
-                   window=s.window, scale=sc.scale, max_context_len=sc.max_context_len,
+                   window=s.window, sinks=s.sinks, scale=sc.scale,
+                   max_context_len=sc.max_context_len,
                    out=out, workspace=ws)
 
     for _ in range(args.warmup):
@@ -319,7 +341,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "num_seqs": s.num_seqs, "q_heads": s.q_heads,
                    "kv_heads": s.kv_heads, "head_dim": s.head_dim, "page_size": s.page_size,
-                   "window": s.window, "seed": sc.seed, "context_sum": int(sc.lens.sum()),
+                   "window": s.window, "sinks": s.sinks, "seed": sc.seed, "context_sum": int(sc.lens.sum()),
                    "kv_bytes_per_step": nb["kv"], "copies": int(len(sc.copy_src)),
                    "stored_rows": int((sc.slot_mapping >= 0).sum()),
                    "cache": ("cold: every timed step starts after a 1 GiB read that evicts "
