@@ -14,6 +14,10 @@ What it computes, and from which passage:
   model", ``PageTable.rows``) and run plain single-query softmax attention in
   float64 over the last ``min(L, W)`` rows (same chapter, the window rule of
   ``PagedChip.generate``).
+* ``attention.prefill`` -- several query tokens per sequence (a prefill
+  chunk or a verify step; the tiny-llm page, section "Prefill with Pages"):
+  each query attends, causally and within the window counted from its own
+  row, the rows a single-query step at its position would.
 * ``kvstore.store_kv`` -- write each new row to its flat slot (the
   mini-sglang page, section on the KV buffer and its store call).
 * ``kvstore.copy_pages`` -- whole-page copy for copy-on-write (silicon chapter

@@ -22,6 +22,14 @@ at logical row ``L - 1``):
 
 ``L == 0`` yields a zero output row.
 
+Several query tokens per sequence (a prefill chunk, or the drafted tokens a
+speculative step verifies; the tiny-llm page "Paged KV Cache", section
+"Prefill with Pages", where a chunk's rows are stored into pages first):
+the ``n`` queries of a sequence of ``L`` rows are its last ``n`` rows, query
+``i`` sits at row ``p = L - n + i`` and attends exactly what a single-query
+step at context ``p + 1`` attends (causal, and within the window counted from
+its own row).  A query with ``p < 0`` (more queries than rows) gets zeros.
+
 Attention sinks (silicon-compiler chapter 15, section "Exercises", exercise 3):
 with ``S`` sink rows and a window ``W`` the step attends the first ``S`` rows
 and the last ``W - S`` rows, so the context is still ``W`` rows once ``L``
@@ -130,4 +138,43 @@ def decode(q_bits: np.ndarray, k_pool_bits: np.ndarray, v_pool_bits: np.ndarray,
         for h in range(q_heads):
             g = kv_head_of(h, q_heads, kv_heads)
             out[n, h] = attend(qs[h], K[:, g, :], V[:, g, :], scale)
+    return out
+
+
+def query_position(L: int, n: int, i: int) -> int:
+    """Row of the ``i``-th of the ``n`` query tokens of a sequence of ``L`` rows."""
+    return L - n + i
+
+
+def prefill(q_bits: np.ndarray, k_pool_bits: np.ndarray, v_pool_bits: np.ndarray,
+            block_tables: np.ndarray, context_lens: np.ndarray, q_start: np.ndarray,
+            page_size: int, window: int, scale: float, dtype: str,
+            rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Float64 output ``[len(rows), q_heads, head_dim]`` for query rows ``rows``.
+
+    ``q_bits`` is ``[num_q, q_heads, head_dim]`` raw bits; the query rows of
+    sequence ``s`` are ``q_start[s] .. q_start[s + 1] - 1``; ``rows`` selects
+    query rows (all by default).
+    """
+    num_q, q_heads, head_dim = q_bits.shape
+    kv_heads = k_pool_bits.shape[2]
+    assert q_heads % kv_heads == 0 and k_pool_bits.shape[3] == head_dim
+    q_start = np.asarray(q_start, dtype=np.int64)
+    B = len(q_start) - 1
+    assert q_start[0] == 0 and q_start[B] == num_q and np.all(np.diff(q_start) >= 0)
+    rows = list(range(num_q)) if rows is None else list(rows)
+    out = np.zeros((len(rows), q_heads, head_dim), dtype=np.float64)
+    for n_out, r in enumerate(rows):
+        s = int(np.searchsorted(q_start, r, side="right")) - 1
+        n = int(q_start[s + 1] - q_start[s])
+        p = query_position(int(context_lens[s]), n, r - int(q_start[s]))
+        if p < 0:
+            continue
+        lo, hi = live_rows(p + 1, window)
+        K = gather(k_pool_bits, block_tables[s], lo, hi, dtype)
+        V = gather(v_pool_bits, block_tables[s], lo, hi, dtype)
+        qs = to_f64(q_bits[r], dtype)
+        for h in range(q_heads):
+            g = kv_head_of(h, q_heads, kv_heads)
+            out[n_out, h] = attend(qs[h], K[:, g, :], V[:, g, :], scale)
     return out

@@ -38,6 +38,13 @@ def expected_step(sc, seqs=None, k_pool_bits=None, v_pool_bits=None):
     vp = bits(sc.v_pool) if v_pool_bits is None else v_pool_bits
     kp, vp = oracle.kvstore.copy_pages(kp, vp, ints(sc.copy_src), ints(sc.copy_dst))
     kp, vp = oracle.kvstore.store_kv(kp, vp, bits(sc.k_new), bits(sc.v_new), ints(sc.slot_mapping))
+    if sc.q_start is not None:
+        # several query tokens per sequence; `seqs` then selects query rows
+        out = oracle.attention.prefill(
+            bits(sc.q), table_view(kp, sc.table_page_size), table_view(vp, sc.table_page_size),
+            ints(sc.block_tables), ints(sc.context_lens), ints(sc.q_start),
+            sc.table_page_size, sc.spec.window, sc.scale, dt, rows=seqs)
+        return kp, vp, out
     out = oracle.attention.decode(
         bits(sc.q), table_view(kp, sc.table_page_size), table_view(vp, sc.table_page_size),
         ints(sc.block_tables), ints(sc.context_lens), sc.table_page_size, sc.spec.window,

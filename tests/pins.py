@@ -356,5 +356,101 @@ def pin_sinks():
     return P
 
 
+def _multi_scenarios():
+    out = []
+    for i, (dt, W, P, ql, qh, hq, hkv, d) in enumerate([
+            ("f32", 0, 4, 2, 6, 4, 2, 8), ("bf16", 7, 2, 1, 9, 8, 2, 16),
+            ("bf16", 5, 16, 3, 12, 4, 4, 16), ("f32", 1, 1, 2, 4, 2, 1, 8),
+            ("bf16", 0, 16, 20, 40, 8, 2, 16)]):
+        out.append(workloads.build(workloads.Spec(
+            name=f"multi{i}", dtype=dt, num_seqs=5, q_heads=hq, kv_heads=hkv, head_dim=d,
+            page_size=P, window=W, len_lo=1, len_hi=60, q_lo=ql, q_hi=qh, pool_factor=1.5),
+            300 + i, keep_source=True))
+    return out
+
+
+def pin_prefill():
+    """Several query tokens per sequence (the tiny-llm page, "Prefill with Pages"):
+    each query equals brute force, and SDPA with a causal window mask written out
+    here, over the unpaged rows; one query per sequence is the decode step;
+    changing the row after a query leaves that query bit-equal and changes the
+    next; queries before row 0 give zeros."""
+    P = []
+    A = oracle.attention
+    for sc in _multi_scenarios():
+        _, _, out = expected_step(sc)
+        W = sc.spec.window
+        qs = ints(sc.q_start)
+        qf = sc.q.to(torch.float64)
+        for s in range(sc.spec.num_seqs):
+            L, n, l0 = int(sc.lens[s]), int(sc.nq[s]), int(sc.lo[s])
+            k = sc.k_src[s].to(torch.float64)
+            v = sc.v_src[s].to(torch.float64)
+            pos = [L - n + i for i in range(n)]
+            for i, p in enumerate(pos):
+                a = max(p + 1 - W, 0) if W > 0 else 0
+                ref = np.array(brute_attention(qf[qs[s] + i].tolist(), k[a - l0:p + 1 - l0].tolist(),
+                                               v[a - l0:p + 1 - l0].tolist(), sc.scale,
+                                               sc.spec.q_heads, sc.spec.kv_heads))
+                err = float(np.max(np.abs(ref - out[qs[s] + i])))
+                if not err <= TOL:
+                    P.append(f"{sc.spec.name} seq {s} query {i}: vs brute force {err:.3g}")
+            if n == 0:
+                continue
+            # SDPA with an explicit boolean mask: key row t (absolute) visible to query p
+            t = torch.arange(l0, L)[None, :]
+            pp = torch.tensor(pos)[:, None]
+            mask = (t <= pp) & ((t > pp - W) if W > 0 else torch.ones_like(t, dtype=torch.bool))
+            qq = qf[qs[s]:qs[s] + n].permute(1, 0, 2)[None].contiguous()
+            kk = k.permute(1, 0, 2)[None].contiguous()
+            vv = v.permute(1, 0, 2)[None].contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, kk, vv, attn_mask=mask, scale=sc.scale, enable_gqa=True)[0].permute(1, 0, 2)
+            err = float(np.max(np.abs(ref.numpy() - out[qs[s]:qs[s] + n])))
+            if not err <= TOL:
+                P.append(f"{sc.spec.name} seq {s}: vs SDPA with a causal window mask {err:.3g}")
+    # one query per sequence is the decode step (bit-equal)
+    sc = workloads.make_config(1, keep_source=True)
+    kp, vp, dec = expected_step(sc)
+    B = sc.spec.num_seqs
+    got = A.prefill(bits(sc.q), kp, vp, ints(sc.block_tables), ints(sc.context_lens),
+                    np.arange(B + 1), sc.spec.page_size, 0, sc.scale, "f32")
+    if not np.array_equal(got, dec):
+        P.append("one query per sequence differs from the decode step")
+    # causality: rewrite the key and value of the row right after query i
+    sc = _multi_scenarios()[1]
+    kp, vp, out = expected_step(sc)
+    s = int(np.argmax(sc.nq))
+    n, L = int(sc.nq[s]), int(sc.lens[s])
+    q0 = int(ints(sc.q_start)[s])
+    bt = ints(sc.block_tables)
+    Pg = sc.spec.page_size
+    for i in range(n - 1):
+        r = L - n + i + 1
+        k2, v2 = kp.copy(), vp.copy()
+        k2[bt[s, r // Pg], r % Pg] ^= np.uint16(0x8000)      # negate the row
+        v2[bt[s, r // Pg], r % Pg] ^= np.uint16(0x8000)
+        o2 = A.prefill(bits(sc.q), k2, v2, bt, ints(sc.context_lens), ints(sc.q_start), Pg,
+                       sc.spec.window, sc.scale, "bf16")
+        if not np.array_equal(o2[:q0 + i + 1], out[:q0 + i + 1]):
+            P.append(f"query {i} saw the row after it")
+        if np.max(np.abs(o2[q0 + i + 1] - out[q0 + i + 1])) < 1e-6:
+            P.append(f"query {i + 1} did not see its own row")
+    # more queries than rows: the first ones sit before row 0 and give zeros
+    sc = workloads.make_config(1, keep_source=True)
+    kp, vp, _ = expected_step(sc)
+    q = bits(sc.q)[[0, 0, 1, 2, 3]]
+    got = A.prefill(q, kp, vp, ints(sc.block_tables)[:1], np.array([3]), np.array([0, 5]),
+                    sc.spec.page_size, 0, sc.scale, "f32")
+    if np.any(got[:2] != 0):
+        P.append("queries before row 0 must give zeros")
+    for i in range(3):
+        d = A.decode(q[2 + i:3 + i], kp, vp, ints(sc.block_tables)[:1], np.array([i + 1]),
+                     sc.spec.page_size, 0, sc.scale, "f32")
+        if not np.array_equal(got[2 + i], d[0]):
+            P.append(f"query {2 + i} of 5 over 3 rows must be the step at context {i + 1}")
+    return P
+
+
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_window, pin_placement,
-            pin_slot_table, pin_store, pin_copy, pin_sinks]
+            pin_slot_table, pin_store, pin_copy, pin_sinks, pin_prefill]

@@ -14,6 +14,7 @@ from oracle import kvstore as S
 
 _live, _gather, _head, _attend = A.live_rows, A.gather, A.kv_head_of, A.attend
 _rows, _gather_rows = A.attended_rows, A.gather_rows
+_qpos = A.query_position
 _store, _copy = S.store_kv, S.copy_pages
 
 
@@ -96,6 +97,10 @@ MUTANTS = {
     "sinks keep one row too many": (A, "attended_rows", lambda L, W, S=0: _rows(L, W, S + 1 if 0 < S < W - 1 else S)),
     "window beside the sinks too long": (A, "attended_rows", _sinks_window_too_long),
     "sink gather reads one row twice": (A, "gather_rows", _gather_rows_first_dup),
+    "queries placed at the chunk start": (A, "query_position", lambda L, n, i: i),
+    "queries one row late": (A, "query_position", lambda L, n, i: _qpos(L, n, i) + 1),
+    "queries one row early": (A, "query_position", lambda L, n, i: _qpos(L, n, i) - 1),
+    "every query at the chunk end": (A, "query_position", lambda L, n, i: L - 1),
 }
 
 

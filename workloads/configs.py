@@ -53,6 +53,8 @@ class Spec:
     page_size: int = 16
     window: int = 0                # 0: attend the whole context
     sinks: int = 0                 # rows at the start kept besides the window (0 <= sinks < window)
+    q_lo: int = 1                  # query tokens per sequence, uniform in [q_lo, q_hi] and at
+    q_hi: int = 1                  # most L: a prefill chunk or a verify step when above 1
     lens: Optional[tuple] = None   # explicit context lengths (include the new token)
     len_dist: str = "uniform"      # "uniform" | "lognormal" (when lens is None)
     len_lo: int = 1                # uniform: low bound; lognormal: median
@@ -143,6 +145,10 @@ class Scenario:
     k_src: Optional[List[torch.Tensor]] = None
     v_src: Optional[List[torch.Tensor]] = None
     shared_pages: int = 0            # pages of the shared prefix (mapped by every sequence)
+    # several query tokens per sequence: q, k_new, v_new and slot_mapping have one row per
+    # query token; those of sequence s are rows q_start[s] .. q_start[s+1]-1 (int32 [B+1])
+    q_start: Optional[torch.Tensor] = None
+    nq: Optional[np.ndarray] = None  # int64 [B], query tokens per sequence
 
     @property
     def table_num_pages(self) -> int:
@@ -186,9 +192,16 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
     assert spec.q_heads % Hkv == 0
     lens = _draw_lens(spec, rng)
     assert (lens >= 0).all()
+    multi = spec.q_hi > 1
+    nq = np.minimum(lens, 1)
+    if multi:
+        # several query tokens per sequence: its last nq rows are new, stored by the step
+        assert not spec.prefix_len and not spec.sinks and 1 <= spec.q_lo <= spec.q_hi
+        nq = np.minimum(rng.integers(spec.q_lo, spec.q_hi + 1, size=B), lens)
     if spec.prefix_len:
         assert W == 0 and spec.prefix_len % P == 0 and (lens > spec.prefix_len).all()
-    lo = np.maximum(lens - W, 0) if W > 0 else np.zeros_like(lens)
+    # first row attended by the first query (row L - nq)
+    lo = np.maximum(lens - nq + 1 - W, 0) if W > 0 else np.zeros_like(lens)
     S = spec.sinks
     if S:
         assert 0 < S < W and not spec.prefix_len and not spec.sibling_cow
@@ -268,10 +281,38 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
         v_pool[pg, r % P] = prefix_v
 
     k_src, v_src = ([], []) if keep_source else (None, None)
-    k_new = torch.zeros(B, Hkv, D, dtype=tdt, device=device)
-    v_new = torch.zeros(B, Hkv, D, dtype=tdt, device=device)
-    slots = np.full(B, -1, dtype=np.int64)
-    for s in range(B):
+    if multi:
+        num_q = int(nq.sum())
+        q_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int64)
+        k_new = torch.zeros(num_q, Hkv, D, dtype=tdt, device=device)
+        v_new = torch.zeros(num_q, Hkv, D, dtype=tdt, device=device)
+        slots = np.full(num_q, -1, dtype=np.int64)
+        for s in range(B):
+            L, l0, n = int(lens[s]), int(lo[s]), int(nq[s])
+            kr = randn(L - l0, Hkv, D)
+            vr = randn(L - l0, Hkv, D)
+            if L - n > l0:                        # rows before the chunk go into the pool
+                r = torch.arange(l0, L - n)
+                pg = torch.tensor([seq_pages[s][int(j)] for j in (r // P).tolist()],
+                                  device=device, dtype=torch.long)
+                off = (r % P).to(device)
+                k_pool[pg, off] = kr[:L - n - l0]
+                v_pool[pg, off] = vr[:L - n - l0]
+            q0 = int(q_start[s])
+            k_new[q0:q0 + n] = kr[L - n - l0:]
+            v_new[q0:q0 + n] = vr[L - n - l0:]
+            for i in range(n):
+                t = L - n + i
+                slots[q0 + i] = post_pages[s][t // P] * P + t % P
+            if keep_source:
+                k_src.append(kr.cpu())
+                v_src.append(vr.cpu())
+        q = randn(num_q, spec.q_heads, D)
+    else:
+        k_new = torch.zeros(B, Hkv, D, dtype=tdt, device=device)
+        v_new = torch.zeros(B, Hkv, D, dtype=tdt, device=device)
+        slots = np.full(B, -1, dtype=np.int64)
+    for s in range(B if not multi else 0):
         L, l0 = int(lens[s]), int(lo[s])
         if L == 0:
             if keep_source:
@@ -317,7 +358,8 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
             else:
                 k_src.append(kr.cpu())
                 v_src.append(vr.cpu())
-    q = randn(B, spec.q_heads, D)
+    if not multi:
+        q = randn(B, spec.q_heads, D)
 
     if spec.slot_table:
         stride = spec.slot_stride or _align32(int(lens.max()))
@@ -345,7 +387,8 @@ def build(spec: Spec, seed: int, device: str = "cpu", keep_source: bool = False)
         context_lens=i32(lens), q=q, k_new=k_new, v_new=v_new, slot_mapping=i32(slots),
         copy_src=i32([c[0] for c in copies]), copy_dst=i32([c[1] for c in copies]),
         scale=scale, max_context_len=int(lens.max()) if B else 0,
-        k_src=k_src, v_src=v_src, shared_pages=n_shared)
+        k_src=k_src, v_src=v_src, shared_pages=n_shared,
+        q_start=i32(q_start) if multi else None, nq=nq)
 
 
 def make_config(index: int, seed: Optional[int] = None, device: str = "cpu",
