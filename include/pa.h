@@ -16,7 +16,8 @@
  *                  reached through a per-sequence block table, optionally
  *                  limited to the last W rows (silicon chapter 15, sections
  *                  "The problem" and "The model"; pa_decode_sinks also keeps
- *                  the first rows, "Exercises"; the dense result it must
+ *                  the first rows, "Exercises"; pa_prefill takes several
+ *                  query tokens per sequence; the dense result it must
  *                  equal is the checkpoint of the tiny-llm page "Paged KV
  *                  Cache", section "Correctness Checkpoint").
  *
@@ -151,6 +152,38 @@ int pa_decode_sinks(float* out, const void* q, const void* k_pool, const void* v
                     int32_t kv_heads, int32_t head_dim, int32_t num_pages, int32_t page_size,
                     int32_t window, int32_t sinks, int32_t max_context_len, float scale,
                     int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * pa_prefill -- several query tokens per sequence against its cached rows: a
+ * chunk of a prompt (the tiny-llm page "Paged KV Cache", section "Prefill
+ * with Pages": the chunk's rows are stored into pages, here by pa_store_kv,
+ * before its queries attend) or the drafted tokens of a speculative step.
+ *   out           fp32 [num_q, q_heads, head_dim], written.
+ *   q             [num_q, q_heads, head_dim], pool dtype.
+ *   q_start       device int32 [num_seqs + 1], nondecreasing, q_start[0] = 0,
+ *                 q_start[num_seqs] = num_q: the query rows of sequence s
+ *                 are q_start[s] .. q_start[s+1] - 1, at most max_q_len.
+ *   context_lens  device int32 [num_seqs]: rows of each sequence including
+ *                 its n query tokens, whose K/V rows must already be stored;
+ *                 the queries are its last n rows.
+ *   Query i of a sequence (0 <= i < n) sits at row p = L - n + i and attends
+ *   rows [p + 1 - min(p + 1, W), p + 1) with a window W > 0, else [0, p + 1):
+ *   causal, the window counted from its own row.  A query with p < 0 (more
+ *   queries than rows) gets a zero row.  n = 1 everywhere is pa_decode.
+ *   max_q_len     host upper bound on the query tokens of one sequence (sizes
+ *                 the grid and the workspace); rows beyond it are not written.
+ *   Every other argument, the workspace rules (zeros before the first use,
+ *   left ready by every call; no overlapping calls on one workspace) and the
+ *   supported shapes are those of pa_decode; there are no sink rows here.
+ *   Errors: PA_EINVAL also for num_q > 0 with num_seqs = 0 or max_q_len <= 0.
+ */
+int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_pool,
+               const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+               const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
+               int32_t max_q_len, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+               int32_t num_pages, int32_t page_size, int32_t window, int32_t max_context_len,
+               float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
+               void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,9 @@ SIGNATURES = {
     "pa_decode_sinks": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                        _I, _I, ctypes.c_float, _I, _P,
                                        ctypes.POINTER(ctypes.c_size_t), _P]),
+    "pa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                  _I, _I, _I, ctypes.c_float, _I, _P,
+                                  ctypes.POINTER(ctypes.c_size_t), _P]),
 }
 
 _lib = None

@@ -24,6 +24,13 @@ struct DecodeArgs {
   float* ws_acc;               // partial accumulators, head_dim floats each
   int* ws_arrive;              // streaming path: per-range arrival counters, zero between calls
   int total_waves;             // streaming path: wavefronts sharing the tile list
+  // Several query tokens per sequence (prefill chunk, verify step).  Streaming path: the
+  // query rows of sequence s are q_start[s] .. q_start[s+1]-1 of q and out (num_q rows,
+  // at most max_q per sequence).  Other paths: every query row is a row of its own, with
+  // its sequence in row_seq and its context (its position + 1) in ctx.
+  const int32_t* q_start;
+  int num_q, max_q;
+  const int32_t* row_seq;      // nullptr: row s reads the table row of sequence s
 };
 
 // Rows attended by a sequence with `ctx` rows: [lo, L) with L = ctx clamped to

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   chunk_span(c, L, sl, lo, a.chunk, t_begin, t_end);
   const int j0 = t_begin >> lp;
   const int nj = ((t_end - 1) >> lp) - j0 + 1;
-  const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
+  const int32_t* btr = a.block_tables + (size_t)(a.row_seq ? a.row_seq[s] : s) * a.bt_stride;
   for (int i = tid; i < nj; i += 64 * NW) {
     const int pg = btr[j0 + i];
     s_pages[i] = (pg >= 0 && pg < a.num_pages) ? pg : -1;

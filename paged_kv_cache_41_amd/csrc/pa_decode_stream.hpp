@@ -9,8 +9,7 @@
 // can cross segment boundaries; the pipeline crosses them too.
 //
 // Every workgroup first turns the context lengths into per-sequence tile counts and an
-// exclusive prefix sum in LDS (workgroup 0 also stores it for the merge kernel).  Each
-// wavefront then runs a three-stage software pipeline over its tiles: the block-table
+// exclusive prefix sum in LDS.  Each wavefront then runs a three-stage software pipeline over its tiles: the block-table
 // entry of tile i+3 (one per lane, for token t0 + lane % 16), the K and V rows of tile
 // i+2, and the compute of tile i.  All loads are unconditional: a row outside the
 // attended range or behind an unmapped entry is read from a clamped address inside the
@@ -34,7 +33,14 @@
 // enough); the accumulators are fp32.  A segment that starts and ends inside one
 // wavefront writes its output directly; the first and last segment of a range may be
 // cut and are written as partial (max, sum, accumulator) to one of two slots of that
-// wavefront, which the merge kernel combines in a fixed order.
+// wavefront; the wavefront that finishes a cut segment's last piece combines its pieces in
+// a fixed order.
+//
+// Several query tokens per sequence (MULTI): the 16 score columns are 16 / G consecutive
+// query tokens times the G heads of the group, so a segment is (block of query tokens,
+// kv head) and covers the rows the block's first query may attend up to its last query's
+// own row; each column is masked to its own query's rows (causal, window counted from
+// that query).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,7 +89,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // Position of a tile in the flattened list, with the fields of its segment.
 struct Cur {
-  int s, g, k;      // sequence, kv head, tile within the segment
+  int s, g, k;      // sequence (block of query tokens with MULTI), kv head, tile within it
+  int tr;           // block-table row
   int tiles;        // tiles of the segment
   int sl, lo, L;    // attended rows [0, sl) and [lo, L)
   int sk;           // tiles of the sink rows: tiles 0 .. sk-1 start at rows 0, 16, ...
@@ -144,7 +151,8 @@ enum : int {
   IDLE = 16,         // past the end of the range: loaded (a repeat) but not computed
 };
 struct Desc {
-  int s, g;          // sequence, kv head
+  int s, g;          // sequence (block of query tokens with MULTI), kv head
+  int tr;            // block-table row
   int t0;            // first row of the tile
   int sl, lo, L;     // attended rows [0, sl) and [lo, L) of the sequence
   int flags;
@@ -154,9 +162,48 @@ struct Desc {
 __shared__ int st_cum[BMAX + 1];   // tiles of sequences before s (st_cum[B] = all)
 __shared__ int st_len[BMAX];       // clamped context length
 __shared__ int st_scan[NW];       // wavefront totals of the scan
+// MULTI: per block of query tokens, its sequence, first query row, position of its first
+// query (negative when the sequence has more queries than rows), tokens and first key row
+__shared__ int st_seq[BMAX];
+__shared__ int st_q0[BMAX];
+__shared__ int st_p0[BMAX];
+__shared__ int st_nt[BMAX];
+__shared__ int st_lo[BMAX];
+
+// Exclusive prefix sum over LDS counts arr[0..n) by the whole workgroup; arr[n] = total.
+__device__ __forceinline__ void wg_exclusive_scan(int* arr, int n, int tid, int lane, int w) {
+  const int per = (n + 64 * NW - 1) / (64 * NW);
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int x = tid * per + i;
+    if (x < n) local += arr[x];
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) st_scan[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += st_scan[i];
+  int run = base + incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int x = tid * per + i;
+    if (x < n) {
+      const int t = arr[x];
+      arr[x] = run;
+      run += t;
+    }
+  }
+  if (tid == 64 * NW - 1) arr[n] = base + incl;
+  __syncthreads();
+}
 
 // The front of a wavefront's pipeline: walks its range one tile per step, then stays on
 // the last tile, marked idle.
+template <bool MULTI>
 struct Front {
   Cur f;
   int rem;            // tiles of the range from the front on (1: the front is on its last)
@@ -167,6 +214,15 @@ struct Front {
   __device__ __forceinline__ void seg_fields() {
     f.tiles = uni(st_cum[f.s + 1] - st_cum[f.s]);
     f.L = uni(st_len[f.s]);
+    if constexpr (MULTI) {
+      f.tr = uni(st_seq[f.s]);
+      f.sl = 0;
+      f.lo = uni(st_lo[f.s]);
+      f.sk = 0;
+      f.t0base = (f.lo >> 4) << 4;
+      return;
+    }
+    f.tr = f.s;
     const bool cut = window > 0 && f.L > window;
     f.sl = cut ? sinks : 0;
     f.lo = cut ? f.L - window + sinks : 0;
@@ -205,6 +261,7 @@ struct Front {
   __device__ __forceinline__ Desc desc() const {
     Desc d;
     d.s = f.s;
+    d.tr = f.tr;
     d.g = f.g;
     d.t0 = f.k * TILE + (f.k >= f.sk ? f.t0base : 0);
     d.sl = f.sl;
@@ -227,15 +284,68 @@ struct Front {
   }
 };
 
-template <int DEPTH, bool PAGE_TILES>
+template <int DEPTH, bool PAGE_TILES, bool MULTI>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int B = a.num_seqs;
   const int Hkv = a.kv_heads;
   const int G = a.group;
+  // score columns in use: the G heads, or (MULTI) 16 / G query tokens of G heads each
+  const int C = MULTI ? 16 : G;
+  const int lg = MULTI ? 31 - __clz(G) : 0;   // G is a power of two with MULTI
+  int B = a.num_seqs;                         // segments per kv head: sequences or blocks
 
+  if constexpr (MULTI) {
+    // ---- blocks of 16 / G query tokens: counts per sequence, prefix sum, block records,
+    // then tile counts per block and their prefix sum ----------------------------------
+    const int tpb = 16 >> lg;
+    for (int s = tid; s < B; s += 64 * NW) {
+      const int q0 = a.q_start[s];
+      int n = a.q_start[s + 1] - q0;
+      if (q0 < 0 || q0 > a.num_q) n = 0;
+      n = max(0, min(min(n, a.num_q - q0), a.max_q));
+      st_cum[s] = (n + tpb - 1) / tpb;
+    }
+    __syncthreads();
+    wg_exclusive_scan(st_cum, B, tid, lane, w);
+    const int VB = st_cum[B];
+    for (int s = tid; s < B; s += 64 * NW) {
+      const int base = st_cum[s], nb = st_cum[s + 1] - base;
+      const int q0 = a.q_start[s];
+      const int n = nb > 0 ? max(0, min(min(a.q_start[s + 1] - q0, a.num_q - q0), a.max_q)) : 0;
+      const int ctx = a.ctx[s];
+      const int L = ctx > 0 ? (ctx < a.max_ctx ? ctx : a.max_ctx) : 0;
+      for (int b = 0; b < nb; ++b) {
+        const int v = base + b;
+        const int nt = min(tpb, n - b * tpb);
+        const int p0 = L - n + b * tpb;          // position of the block's first query
+        const int kend = max(p0 + nt, 0);        // one past the last query's row
+        const int lo = a.window > 0 ? max(p0 + 1 - a.window, 0) : 0;
+        st_seq[v] = s;
+        st_q0[v] = q0 + b * tpb;
+        st_p0[v] = p0;
+        st_nt[v] = nt;
+        st_lo[v] = lo;
+        st_len[v] = kend;
+      }
+    }
+    __syncthreads();
+    // st_cum is read above by every thread before any rewrites it
+    for (int v = tid; v < VB; v += 64 * NW) {
+      const int kend = st_len[v], lo = st_lo[v];
+      st_cum[v] = kend > 0 ? ((kend - 1) >> 4) - (lo >> 4) + 1 : 0;
+    }
+    __syncthreads();
+    wg_exclusive_scan(st_cum, VB, tid, lane, w);
+    B = VB;
+    // query rows of blocks with nothing to attend are zero
+    for (int v = blockIdx.x; v < B; v += gridDim.x) {
+      if (st_cum[v + 1] != st_cum[v]) continue;
+      float* out = a.out + (size_t)st_q0[v] * a.q_heads * HD;
+      for (int i = tid; i < st_nt[v] * a.q_heads * HD; i += 64 * NW) out[i] = 0.f;
+    }
+  } else {
   // ---- per-sequence tile counts and their exclusive prefix sum --------------------------
   {
     const int per = (B + 64 * NW - 1) / (64 * NW);
@@ -282,6 +392,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     float* out = a.out + (size_t)s * a.q_heads * HD;
     for (int i = tid; i < a.q_heads * HD; i += 64 * NW) out[i] = 0.f;
   }
+  }
 
   // ---- this wavefront's range ------------------------------------------------------------
   const int T = uni(Hkv * st_cum[B]);
@@ -301,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  Front fr;
+  Front<MULTI> fr;
   fr.B = B;
   fr.Hkv = Hkv;
   fr.window = a.window;
@@ -322,11 +433,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     if constexpr (PAGE_TILES) {
       const int t = d.t0 < d.sl ? d.t0 : min(max(d.t0, d.lo), d.L - 1);
       // num_seqs * bt_stride < 2^31 on this path, so the index fits one scalar register
-      return bt_const[uni(d.s * a.bt_stride + (t >> lp))];
+      return bt_const[uni(d.tr * a.bt_stride + (t >> lp))];
     } else {
       const int tc = d.t0 + col;
       const int t = tc < d.sl ? tc : min(max(tc, d.lo), d.L - 1);
-      return a.block_tables[(size_t)d.s * a.bt_stride + (t >> lp)];
+      return a.block_tables[(size_t)d.tr * a.bt_stride + (t >> lp)];
     }
   };
 
@@ -346,9 +457,16 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     if (d.flags & (RANGE_FIRST | SEG_FIRST)) {
       // the query rows of the group, fetched with the tile so that waiting for them is
       // waiting for this tile; lanes past the group read head 0 and are zeroed later
+      size_t qr;
+      if constexpr (MULTI) {
+        // column col: query token col / G of the block, head col % G of the group
+        const int tq = (col >> lg) < st_nt[d.s] ? (col >> lg) : 0;
+        qr = (size_t)(st_q0[d.s] + tq) * a.q_heads + (size_t)d.g * G + (col & (G - 1));
+      } else {
+        qr = (size_t)d.s * a.q_heads + (size_t)d.g * G + (col < G ? col : 0);
+      }
       const uint4* qrow = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(a.q) +
-          ((size_t)d.s * a.q_heads + (size_t)d.g * G + (col < G ? col : 0)) * HD + grp * 32);
+          reinterpret_cast<const uint16_t*>(a.q) + qr * HD + grp * 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.q[j] = qrow[j];
     }
@@ -396,8 +514,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   f32x4 oacc[8];
   bool first_seg = true;     // the segment being computed is the first of the range
   bool started_here = false; // ... and its tile 0 lies in this range
-  // partial area: the (max, sum) pair of every slot and head, then their accumulators
-  const uint32_t nslots = (uint32_t)a.total_waves * 2 * G;
+  // this lane's score column is in use; (MULTI) the rows its query may attend are
+  // (pc_lo, pc]
+  bool cval = col < G;
+  int pc = 0, pc_lo = 0;
+  // partial area: the (max, sum) pair of every slot and column, then their accumulators
+  const uint32_t nslots = (uint32_t)a.total_waves * 2 * C;
   const DevBuf part(a.ws_ml, nslots * (2 + HD) * 4);
   auto ml_off = [&](uint32_t idx) { return idx * 8; };
   auto acc_off = [&](uint32_t idx) { return nslots * 8 + idx * HD * 4; };
@@ -408,8 +530,13 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   auto begin_segment = [&](const Desc& d, const Tile& Tl) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
+    if constexpr (MULTI) {
+      cval = (col >> lg) < st_nt[d.s];
+      pc = st_p0[d.s] + (col >> lg);
+      pc_lo = a.window > 0 ? pc - a.window : (-0x7fffffff - 1);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(col < G ? Tl.q[j] : zero);
+    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(cval ? Tl.q[j] : zero);
     m_ref = -INFINITY;
     l_run = 0.f;
 #pragma unroll
@@ -426,12 +553,19 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     for (int r = 0; r < 4; ++r) lr[r] = __shfl(lt, 4 * grp + r, 64);
     if (complete) {
       float* out = a.out + ((size_t)d.s * a.q_heads + (size_t)d.g * G) * HD + col * 8;
+      int ncols = G;
+      if constexpr (MULTI) {
+        out = a.out + ((size_t)st_q0[d.s] * a.q_heads + (size_t)d.g * G) * HD + col * 8;
+        ncols = st_nt[d.s] << lg;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
-        if (h < G) {
+        if (h < ncols) {
           const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;
-          float4* o = reinterpret_cast<float4*>(out + (size_t)h * HD);
+          // MULTI: column h is head h % G of query token h / G (rows q_heads apart)
+          const size_t row = MULTI ? (size_t)(h >> lg) * a.q_heads + (h & (G - 1)) : (size_t)h;
+          float4* o = reinterpret_cast<float4*>(out + row * HD);
           o[0] = make_float4(oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv);
           o[1] = make_float4(oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv);
         }
@@ -441,12 +575,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
       // through to the point where every compute unit reads it)
       const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
-      if (lane < G) part.store2(ml_off((uint32_t)pi * G + lane), make_float2(m_ref, lt));
+      if (lane < C) part.store2(ml_off((uint32_t)pi * C + lane), make_float2(m_ref, lt));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
-        if (h < G) {
-          const uint32_t o = acc_off((uint32_t)pi * G + h) + col * 32;
+        if (h < C) {
+          const uint32_t o = acc_off((uint32_t)pi * C + h) + col * 32;
           part.store4(o, make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]));
           part.store4(o + 16, make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]));
         }
@@ -480,14 +614,18 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = (Tl.valid >> (4 * grp + r)) & 1;
+      bool ok = (Tl.valid >> (4 * grp + r)) & 1;
+      if constexpr (MULTI) {
+        const int t = d.t0 + 4 * grp + r;
+        ok = ok && t <= pc && t > pc_lo;
+      }
       sv[r] = ok ? sc[r] * a.qscale : -INFINITY;
       mt = fmaxf(mt, sv[r]);
     }
     // raise the reference when some head's tile max passes it by more than RESCALE_T;
     // this lane's own max decides whether any does, so the cross-lane max is only taken
     // on the (rare) raise
-    if (__ballot(col < G && mt > m_ref + RESCALE_T) != 0) {
+    if (__ballot(cval && mt > m_ref + RESCALE_T) != 0) {
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float mn = fmaxf(m_ref, mt);
@@ -505,7 +643,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - ms) : 0.f;
+      p[r] = cval ? __builtin_amdgcn_exp2f(sv[r] - ms) : 0.f;
       l_run += p[r];
     }
     // P as the A operand (row = head col, k = token 4 grp + r), split into a bf16 high
@@ -613,8 +751,13 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     // in range k1 the segment is the first one (slot 0) only if it starts the range
     const int slot1 = seg_start == range_start(T, R, k1) ? 0 : 1;
     float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
+    int ncols = G;
+    if constexpr (MULTI) {
+      out = a.out + ((size_t)st_q0[s] * a.q_heads + (size_t)g * G) * HD;
+      ncols = st_nt[s] << lg;
+    }
     const int c4 = (lane & 31) * 4;
-    for (int h = lane >> 5; h < G; h += 2) {
+    for (int h = lane >> 5; h < ncols; h += 2) {
       float M = -INFINITY, den = 0.f;
       float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int k0 = k1; k0 <= k2; k0 += COMBINE_BATCH) {
@@ -624,8 +767,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
           const size_t pi = (size_t)k * 2 + (k == k1 ? slot1 : 0);
-          ml[b] = part.load2(ml_off((uint32_t)pi * G + h));
-          x[b] = part.load4(acc_off((uint32_t)pi * G + h) + c4 * 4);
+          ml[b] = part.load2(ml_off((uint32_t)pi * C + h));
+          x[b] = part.load4(acc_off((uint32_t)pi * C + h) + c4 * 4);
         }
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
@@ -642,7 +785,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         }
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
-      *reinterpret_cast<float4*>(out + (size_t)h * HD + c4) =
+      const size_t row = MULTI ? (size_t)(h >> lg) * a.q_heads + (h & (G - 1)) : (size_t)h;
+      *reinterpret_cast<float4*>(out + row * HD + c4) =
           make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
     }
     if (lane == 0)
@@ -652,7 +796,6 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   if (last1) combine(seg1, k1_1, k2_1);
 }
 
-// Tiles of the list at most: every segment covers ceil(n / 16) + 1 tiles at most.
 // Tiles of the whole list at most: max_live attended rows per sequence, of which `sinks`
 // may form a run of their own at the start.
 inline int64_t tiles_bound(int num_seqs, int kv_heads, int max_live, int sinks) {
@@ -669,29 +812,54 @@ inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_
          tiles_bound(num_seqs, kv_heads, max_live, sinks) < ((int64_t)1 << 30);
 }
 
+// Several query tokens per sequence: blocks of 16 / group tokens, each attending at most
+// `keys` rows (the window plus the block's other tokens, or the whole context).
+inline int64_t blocks_bound(int num_seqs, int group, int max_q) {
+  const int tpb = 16 / group;
+  return (int64_t)num_seqs * ((max_q + tpb - 1) / tpb);
+}
+inline int64_t tiles_bound_multi(int num_seqs, int kv_heads, int group, int max_q, int keys) {
+  return blocks_bound(num_seqs, group, max_q) * kv_heads * ((keys + 15) / 16 + 1);
+}
+inline bool eligible_multi(int dtype, int head_dim, int group, int page_size, int num_seqs,
+                           int bt_stride, int kv_heads, int max_q, int keys) {
+  return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
+         (group & (group - 1)) == 0 && page_size > 0 && (page_size & (page_size - 1)) == 0 &&
+         num_seqs >= 1 && max_q >= 1 && blocks_bound(num_seqs, group, max_q) <= BMAX &&
+         (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31) &&
+         tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys) < ((int64_t)1 << 30);
+}
+
 // Workspace: the arrival counters (zero between calls), then per wavefront two partial
-// slots of `group` heads (running max and sum, accumulator).
-inline size_t workspace_bytes(int total_waves, int group) {
-  const size_t slots = (size_t)total_waves * 2 * group;
+// slots of `cols` score columns (running max and sum, accumulator): the group's heads, or
+// 16 with several query tokens per sequence.
+inline size_t workspace_bytes(int total_waves, int cols) {
+  const size_t slots = (size_t)total_waves * 2 * cols;
   const size_t counters = ((size_t)total_waves * 4 + 255) / 256 * 256;
   return counters + slots * 2 * sizeof(float) + slots * HD * sizeof(float);
 }
-inline void carve_workspace(DecodeArgs& a, void* workspace) {
-  const size_t slots = (size_t)a.total_waves * 2 * a.group;
+inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
+  const size_t slots = (size_t)a.total_waves * 2 * cols;
   const size_t counters = ((size_t)a.total_waves * 4 + 255) / 256 * 256;
   a.ws_arrive = reinterpret_cast<int*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counters);
   a.ws_acc = a.ws_ml + slots * 2;
 }
 
-inline int launch(const DecodeArgs& a, hipStream_t st) {
+inline int launch(const DecodeArgs& a, hipStream_t st, bool multi) {
   const unsigned blocks = (unsigned)(a.total_waves / NW);
-  if (a.page_size >= TILE)
-    hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true>), dim3(blocks), dim3(64 * NW), 0,
-                       st, a);
-  else
-    hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false>), dim3(blocks), dim3(64 * NW),
-                       0, st, a);
+  const dim3 grid(blocks), block(64 * NW);
+  if (multi) {
+    if (a.page_size >= TILE)
+      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false, true>), grid, block, 0, st, a);
+  } else {
+    if (a.page_size >= TILE)
+      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true, false>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

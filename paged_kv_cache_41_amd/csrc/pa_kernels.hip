@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   const T* kp = reinterpret_cast<const T*>(a.k_pool);
   const T* vp = reinterpret_cast<const T*>(a.v_pool);
   const size_t row_stride = (size_t)Hkv * D;
-  const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
+  const int32_t* btr = a.block_tables + (size_t)(a.row_seq ? a.row_seq[s] : s) * a.bt_stride;
   int t_begin, t_end;
   chunk_span(c, L, sl, lo, a.chunk, t_begin, t_end);
 
@@ -301,6 +301,49 @@ inline int pick_chunk(int max_live) {
   return c;
 }
 
+// Rows path: one work item per (row, chunk, kv head) on the chunked matrix-core kernel or
+// the VALU kernel, then the merge of rows split over several chunks.
+inline int launch_rows(const DecodeArgs& a, DecodeFn generic, bool fast, int head_dim,
+                       hipStream_t st) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.max_chunks * a.kv_heads;
+  if (blocks * 256 > INT32_MAX) return PA_EUNSUPPORTED;
+  if (fast) {
+    if (mfma::launch(a, st) != 0) return PA_ELAUNCH;
+  } else {
+    hipLaunchKernelGGL(generic, dim3((unsigned)blocks), dim3(64), 0, st, a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  if (a.max_chunks > 1) {
+    const int64_t mb = (int64_t)a.num_seqs * a.q_heads;
+    if (mb > INT32_MAX) return PA_EUNSUPPORTED;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)mb), dim3(128), 0, st, a, head_dim);
+    if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  }
+  return PA_OK;
+}
+
+// Query row r of a prefill chunk as a row of its own: its sequence (the last s with
+// q_start[s] <= r) and its context, position + 1 (0 when it lies before row 0 or outside
+// its sequence's rows).
+__global__ __launch_bounds__(256) void prefill_rows_kernel(const int32_t* q_start,
+                                                           const int32_t* ctx, int num_seqs,
+                                                           int num_q, int max_ctx,
+                                                           int32_t* row_seq, int32_t* row_ctx) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= num_q) return;
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (q_start[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int q0 = q_start[lo], n = q_start[lo + 1] - q0, i = r - q0;
+  const int c = ctx[lo];
+  const int L = c > 0 ? (c < max_ctx ? c : max_ctx) : 0;
+  const int p = L - n + i;
+  row_seq[r] = lo;
+  row_ctx[r] = (i >= 0 && i < n && p >= 0) ? p + 1 : 0;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -442,8 +485,9 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
     a.max_ctx = max_context_len;
     a.qscale = scale * 1.4426950408889634f;
     a.total_waves = (int)waves;
-    stream::carve_workspace(a, workspace);
-    return stream::launch(a, reinterpret_cast<hipStream_t>(stream)) == 0 ? PA_OK : PA_ELAUNCH;
+    stream::carve_workspace(a, workspace, group);
+    return stream::launch(a, reinterpret_cast<hipStream_t>(stream), false) == 0 ? PA_OK
+                                                                               : PA_ELAUNCH;
   }
   a.chunk = pick_chunk(max_live);
   const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
@@ -482,21 +526,7 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
   a.ws_ml = reinterpret_cast<float*>(workspace);
   a.ws_acc = a.ws_ml + 2 * parts;
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int64_t blocks = (int64_t)num_seqs * a.max_chunks * kv_heads;
-  if (blocks * 256 > INT32_MAX) return PA_EUNSUPPORTED;
-  if (fast) {
-    if (mfma::launch(a, st) != 0) return PA_ELAUNCH;
-  } else {
-    hipLaunchKernelGGL(generic, dim3((unsigned)blocks), dim3(64), 0, st, a);
-  }
-  if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
-  if (a.max_chunks > 1) {
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * q_heads)), dim3(128), 0, st, a,
-                       (int)head_dim);
-    if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
-  }
-  return PA_OK;
+  return launch_rows(a, generic, fast, head_dim, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
@@ -508,4 +538,116 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
   return pa_decode_sinks(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens,
                          num_seqs, q_heads, kv_heads, head_dim, num_pages, page_size, window, 0,
                          max_context_len, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
+                          int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
+                          int32_t head_dim, int32_t num_pages, int32_t page_size,
+                          int32_t window, int32_t max_context_len, float scale, int32_t dtype,
+                          void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return PA_EINVAL;
+  if (num_seqs < 0 || num_q < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 ||
+      num_pages <= 0 || page_size <= 0 || bt_stride <= 0)
+    return PA_EINVAL;
+  if (num_q > 0 && (num_seqs == 0 || max_q_len <= 0)) return PA_EINVAL;
+  if (q_heads % kv_heads) return PA_EINVAL;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  if (!(scale == scale)) return PA_EINVAL;
+  const int group = q_heads / kv_heads;
+  const int64_t table_rows = (int64_t)bt_stride * page_size;
+  if (max_context_len <= 0) max_context_len = table_rows > INT32_MAX ? INT32_MAX : (int32_t)table_rows;
+  if ((int64_t)max_context_len > table_rows) return PA_EINVAL;
+  if (group > 16) return PA_EUNSUPPORTED;
+  DecodeFn generic = dtype == PA_F32 ? pick_generic_d<float>(head_dim, group)
+                                     : pick_generic_d<uint16_t>(head_dim, group);
+  if (!generic) return PA_EUNSUPPORTED;
+  if (num_q == 0) {
+    if (!workspace) *workspace_bytes = 0;
+    return PA_OK;
+  }
+  const int max_q = max_q_len < num_q ? max_q_len : num_q;
+  const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.window = window > 0 ? window : 0;
+  a.max_ctx = max_context_len;
+  a.qscale = scale * 1.4426950408889634f;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  // keys one block of 16 / group query tokens may attend
+  const int tpb = 16 / group;
+  const int64_t keys64 = window > 0 ? (int64_t)window + tpb - 1 : (int64_t)max_context_len;
+  const int keys = (int)(keys64 < max_context_len ? keys64 : max_context_len);
+  if (stream::eligible_multi(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
+                             max_q, keys)) {
+    const int64_t tiles_max =
+        stream::tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys);
+    int64_t waves = tiles_max / 22;
+    if (waves > stream_waves_max) waves = stream_waves_max;
+    if (waves < stream::NW) waves = stream::NW;
+    waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
+    const size_t need = stream::workspace_bytes((int)waves, 16);
+    if (!workspace) {
+      *workspace_bytes = need;
+      return PA_OK;
+    }
+    if (*workspace_bytes < need) return PA_EWORKSPACE;
+    if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens)
+      return PA_EINVAL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+        !aligned16(workspace))
+      return PA_EUNSUPPORTED;
+    if ((int64_t)kv_heads * head_dim * 2 * page_size > UINT32_MAX) return PA_EUNSUPPORTED;
+    a.ctx = context_lens;
+    a.num_seqs = num_seqs;
+    a.q_start = q_start;
+    a.num_q = num_q;
+    a.max_q = max_q;
+    a.total_waves = (int)waves;
+    stream::carve_workspace(a, workspace, 16);
+    return stream::launch(a, st, true) == 0 ? PA_OK : PA_ELAUNCH;
+  }
+
+  // every query row as a row of its own: its sequence and context first, then the rows path
+  a.chunk = pick_chunk(max_live);
+  const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
+  if (fast) a.chunk = mfma::chunk_for(num_q, kv_heads, max_live);
+  a.max_chunks = (max_live + a.chunk - 1) / a.chunk;
+  if (a.max_chunks < 1) a.max_chunks = 1;
+  const size_t rows_bytes = ((size_t)num_q * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t parts = (size_t)num_q * q_heads * a.max_chunks;
+  const size_t need = rows_bytes + parts * ((size_t)head_dim + 2) * sizeof(float);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return PA_OK;
+  }
+  if (*workspace_bytes < need) return PA_EWORKSPACE;
+  if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PA_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_EUNSUPPORTED;
+  int32_t* row_seq = reinterpret_cast<int32_t*>(workspace);
+  int32_t* row_ctx = row_seq + num_q;
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3((unsigned)((num_q + 255) / 256)), dim3(256), 0,
+                     st, q_start, context_lens, num_seqs, num_q, max_context_len, row_seq,
+                     row_ctx);
+  if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  a.ctx = row_ctx;
+  a.row_seq = row_seq;
+  a.num_seqs = num_q;
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + rows_bytes);
+  a.ws_acc = a.ws_ml + 2 * parts;
+  return launch_rows(a, generic, fast, head_dim, st);
 }

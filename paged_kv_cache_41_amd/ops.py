@@ -1,4 +1,4 @@
-"""Torch-facing binding of the three C-ABI entry points.
+"""Torch-facing binding of the C-ABI entry points.
 
 Argument marshalling only: shape, dtype, device and contiguity checks, then
 raw device pointers and the current HIP stream go to libpa.so.  Every step of
@@ -142,4 +142,67 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, workspace.data_ptr(),
                  workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    return out
+
+
+def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
+                  window, scale, max_context_len, ws_ptr, ws_size, stream_handle):
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    num_q, hq, _ = (int(x) for x in q.shape)
+    B = int(context_lens.shape[0])
+    lib = _lib.load()
+    size = ctypes.c_size_t(ws_size)
+    _lib.check("pa_prefill", lib.pa_prefill(
+        out.data_ptr() if out is not None else None, q.data_ptr(), q_start.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+        int(block_tables.shape[1]), context_lens.data_ptr(), B, num_q, int(max_q_len), hq, hkv,
+        d, n, P, int(window), int(max_context_len), float(scale), _code(q), ws_ptr,
+        ctypes.byref(size), stream_handle))
+    return size.value
+
+
+def prefill_workspace_bytes(q, q_start, k_pool, v_pool, block_tables, context_lens, *,
+                            max_q_len: int, window: int = 0, max_context_len: int = 0) -> int:
+    """Bytes of device workspace ``prefill`` needs for these operands."""
+    return _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens,
+                         max_q_len, window, 1.0, max_context_len, None, 0, None)
+
+
+def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len: int,
+            window: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """Several query tokens per sequence (``pa_prefill``); returns fp32 ``[num_q, q_heads, head_dim]``.
+
+    ``q`` is ``[num_q, q_heads, head_dim]``; the query rows of sequence ``s`` are
+    ``q_start[s] .. q_start[s+1]-1`` (int32 ``[num_seqs + 1]``, at most
+    ``max_q_len`` per sequence) and are its last rows.  Workspace rules as for
+    ``decode``.
+    """
+    dev = _dev(q, q_start, k_pool, v_pool, block_tables, context_lens)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_q, q_heads, head_dim] in the pool dtype")
+    B = int(context_lens.shape[0])
+    if context_lens.dim() != 1 or q_start.shape != (B + 1,):
+        raise ValueError("context_lens must be [num_seqs] and q_start [num_seqs + 1]")
+    if block_tables.dim() != 2 or block_tables.shape[0] < B:
+        raise ValueError("block_tables must be [>= num_seqs, stride]")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    _i32(q_start, "q_start")
+    if scale is None:
+        scale = d ** -0.5
+    num_q = int(q.shape[0])
+    if out is None:
+        out = torch.empty(num_q, q.shape[1], d, dtype=torch.float32, device=dev)
+    elif out.shape != (num_q, q.shape[1], d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [num_q, q_heads, head_dim]")
+    need = _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
+                         window, scale, max_context_len, None, 0, None)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, window,
+                  scale, max_context_len, workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream(dev, stream))
     return out

@@ -74,6 +74,17 @@ def test_argument_validation_needs_no_gpu():
     assert sink(1024, 4) == _lib.PA_OK and size.value > 0
     with_sinks = size.value
     assert sink(1024, 0) == _lib.PA_OK and size.value <= with_sinks
+    # prefill: no queries is a no-op; queries without sequences or a bound are invalid;
+    # the size query works for the streaming shape and for the rows path (fp32)
+    pre = lambda B, nq, mq, hq, hkv, d, dt: lib.pa_prefill(
+        None, None, None, None, None, None, 256, None, B, nq, mq, hq, hkv, d, 1000, 16, 0, 4096,
+        1.0, dt, None, ctypes.byref(size), None)
+    size.value = 7
+    assert pre(4, 0, 8, 32, 8, 128, 1) == _lib.PA_OK and size.value == 0
+    assert pre(0, 5, 8, 32, 8, 128, 1) == _lib.PA_EINVAL
+    assert pre(4, 5, 0, 32, 8, 128, 1) == _lib.PA_EINVAL
+    assert pre(4, 32, 8, 32, 8, 128, 1) == _lib.PA_OK and size.value > 0
+    assert pre(4, 32, 8, 32, 8, 64, 0) == _lib.PA_OK and size.value > 0
     # store / copy: bad dtype, zero-sized no-ops
     assert lib.pa_store_kv(None, None, None, None, None, 1, 8, 16, 8, 128, 7, None) == _lib.PA_EINVAL
     assert lib.pa_store_kv(None, None, None, None, None, 0, 8, 16, 8, 128, 1, None) == _lib.PA_OK

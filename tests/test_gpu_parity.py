@@ -43,8 +43,13 @@ def gpu_step(sc):
     o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
     kv, vv = decode_views(sc)
-    out = o.decode(sc.q, kv, vv, sc.block_tables, sc.context_lens, window=sc.spec.window,
-                   sinks=sc.spec.sinks, scale=sc.scale, max_context_len=sc.max_context_len)
+    if sc.q_start is not None:
+        out = o.prefill(sc.q, sc.q_start, kv, vv, sc.block_tables, sc.context_lens,
+                        max_q_len=max(int(sc.nq.max()), 1), window=sc.spec.window,
+                        scale=sc.scale, max_context_len=sc.max_context_len)
+    else:
+        out = o.decode(sc.q, kv, vv, sc.block_tables, sc.context_lens, window=sc.spec.window,
+                       sinks=sc.spec.sinks, scale=sc.scale, max_context_len=sc.max_context_len)
     torch.cuda.synchronize()
     return kp0, vp0, out
 
@@ -170,6 +175,92 @@ def test_sinks_equal_window_rows_differ_from_plain_window():
     # between the two calls (more tiles with sinks), so only the rounding order may differ
     assert float(np.max(np.abs(a[~cut] - b[~cut]))) <= 1e-5
     assert (np.max(np.abs(a[cut] - b[cut]), axis=(1, 2)) > 1e-3).all()
+
+
+# Several query tokens per sequence (prefill chunks, verify steps): the chunk's rows are
+# stored by the step, then every query attends causally within its window.
+MULTI = {
+    "verify_g4_p16": dict(_GQA, num_seqs=48, page_size=16, len_lo=1, len_hi=700, q_lo=1,
+                          q_hi=8, spare="nan"),
+    "verify_g4_p16_w64": dict(_GQA, num_seqs=48, page_size=16, window=64, len_lo=1,
+                              len_hi=700, q_lo=2, q_hi=8),
+    "chunk_g4_p16": dict(_GQA, num_seqs=6, page_size=16, len_lo=40, len_hi=400, q_lo=20,
+                         q_hi=90, spare="nan"),
+    "chunk_g4_p16_w40": dict(_GQA, num_seqs=6, page_size=16, window=40, len_lo=40,
+                             len_hi=400, q_lo=20, q_hi=90),
+    "chunk_g1_p8": dict(dtype="bf16", q_heads=8, kv_heads=8, head_dim=128, num_seqs=5,
+                        page_size=8, len_lo=1, len_hi=200, q_lo=1, q_hi=40),
+    "verify_g2_p4_w9": dict(dtype="bf16", q_heads=8, kv_heads=4, head_dim=128, num_seqs=20,
+                            page_size=4, window=9, len_lo=1, len_hi=120, q_lo=1, q_hi=6,
+                            spare="nan"),
+    "verify_g8_slots": dict(dtype="bf16", q_heads=64, kv_heads=8, head_dim=128, num_seqs=16,
+                            page_size=16, len_lo=1, len_hi=500, q_lo=1, q_hi=5,
+                            slot_table=True),
+    "verify_g16_p32_w30": dict(dtype="bf16", q_heads=16, kv_heads=1, head_dim=128,
+                               num_seqs=12, page_size=32, window=30, len_lo=1, len_hi=300,
+                               q_lo=1, q_hi=4),
+    # other paths: every query row as a row of its own
+    "rows_f32_d64": dict(dtype="f32", q_heads=8, kv_heads=2, head_dim=64, num_seqs=8,
+                         page_size=4, window=25, len_lo=1, len_hi=150, q_lo=1, q_hi=12,
+                         spare="nan"),
+    "rows_bf16_g3": dict(dtype="bf16", q_heads=12, kv_heads=4, head_dim=128, num_seqs=10,
+                         page_size=16, len_lo=1, len_hi=400, q_lo=1, q_hi=10),
+    "rows_bf16_d32": dict(dtype="bf16", q_heads=4, kv_heads=2, head_dim=32, num_seqs=10,
+                          page_size=2, window=11, len_lo=1, len_hi=90, q_lo=1, q_hi=9),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI))
+def test_prefill(name):
+    sc = workloads.build(workloads.Spec(name=f"prefill_{name}", pool_factor=1.25,
+                                        **MULTI[name]), 37, device="cuda")
+    assert int(sc.nq.max()) > 1
+    check_step(sc)
+
+
+def test_prefill_many_blocks_rows_path():
+    # 64 sequences of up to 200 query tokens: more blocks than the streaming path takes,
+    # so every query row runs as a row of its own on the chunked matrix-core kernel
+    spec = workloads.Spec(name="prefill_b64_q200", **_GQA, num_seqs=64, page_size=16,
+                          len_lo=150, len_hi=600, q_lo=150, q_hi=200, pool_factor=1.25)
+    sc = workloads.build(spec, 41, device="cuda")
+    rng = np.random.default_rng(4)
+    rows = sorted(set(rng.choice(len(sc.q), 60, replace=False).tolist()) | {0, len(sc.q) - 1})
+    check_step(sc, seqs=rows)
+
+
+def test_prefill_more_queries_than_rows():
+    # contexts shortened below the chunk length: queries before row 0 give zero rows
+    spec = workloads.Spec(name="prefill_short", **_GQA, num_seqs=12, page_size=16, len_lo=1,
+                          len_hi=120, q_lo=4, q_hi=24, pool_factor=1.25)
+    sc = workloads.build(spec, 43, device="cuda")
+    o = ops()
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    ctx = sc.context_lens.clone()
+    ctx[::2] = torch.as_tensor(sc.nq[::2] // 2, device="cuda", dtype=torch.int32)
+    for path in ("stream", "rows"):
+        # the rows path through fp32 would need other pools: force it with a larger bound
+        mq = max(int(sc.nq.max()), 1) if path == "stream" else 2048
+        out = o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, ctx,
+                        max_q_len=mq, scale=sc.scale).cpu().double().numpy()
+        ref = oracle.attention.prefill(bits(sc.q), bits(sc.k_pool), bits(sc.v_pool),
+                                       ints(sc.block_tables), ints(ctx), ints(sc.q_start), 16,
+                                       0, sc.scale, "bf16")
+        assert (ref == 0).all(axis=(1, 2)).any(), "no query before row 0"
+        assert float(np.max(np.abs(out - ref))) <= TOL["bf16"], path
+
+
+def test_prefill_single_token_equals_decode():
+    # one query per sequence: pa_prefill and pa_decode attend the same rows
+    sc = workloads.make_config(2, device="cuda")
+    o = ops()
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    B = sc.spec.num_seqs
+    qs = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    a = o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens, scale=sc.scale)
+    b = o.prefill(sc.q, qs, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+                  max_q_len=1, scale=sc.scale)
+    assert float((a - b).abs().max()) <= 1e-5
 
 
 @pytest.mark.parametrize("seed", range(40))
