@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 
 
 def parse():
@@ -40,6 +41,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--q-len", type=int, default=1,
+                   help="query tokens per sequence (a verify step or a prefill chunk): the last "
+                        "N rows of each context, through pa_prefill")
     p.add_argument("--sinks", type=int, default=0,
                    help="attention-sink rows kept besides the window (workloads with a window)")
     p.add_argument("--warm-steps", type=int, default=None,
@@ -82,10 +86,26 @@ def decode_bytes(sc) -> dict:
         first = sc.lo // tps
         last = np.where(sc.lens > 0, (sc.lens - 1) // tps, first - 1)
         table = int((4 * (last - first + 1)).clip(min=0).sum())
-    q = s.num_seqs * s.q_heads * s.head_dim * elt
-    out = s.num_seqs * s.q_heads * s.head_dim * 4
-    return {"kv": kv, "total": kv + table + q + out + 4 * s.num_seqs,
-            "unique_kv": None}
+    nq = len(sc.q)
+    q = nq * s.q_heads * s.head_dim * elt
+    out = nq * s.q_heads * s.head_dim * 4
+    extra = 4 * s.num_seqs + (4 * (s.num_seqs + 1) if sc.q_start is not None else 0)
+    return {"kv": kv, "total": kv + table + q + out + extra, "unique_kv": None}
+
+
+def attention_flops(sc) -> int:
+    """Multiply-adds x 2 of scores and P.V: 4 head_dim flops per (query head, attended row)."""
+    s = sc.spec
+    W = s.window
+    if sc.q_start is None:
+        keys = (sc.lens - sc.lo).sum()
+    else:
+        keys = 0
+        for L, n in zip(sc.lens.tolist(), sc.nq.tolist()):
+            for i in range(n):
+                p = L - n + i
+                keys += min(p + 1, W) if W > 0 else p + 1
+    return int(4 * s.head_dim * s.q_heads * keys)
 
 
 def unique_kv_bytes(sc) -> int:
@@ -184,8 +204,13 @@ def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
     with threadpool_limits(limits=1):
         while time.perf_counter() - t0 < budget_s:
             i = done % s.num_seqs
-            oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype, seqs=[i],
-                                    sinks=s.sinks)
+            if sc.q_start is not None:
+                qs = sc.q_start.cpu().numpy()
+                oracle.attention.prefill(q, kp, vp, bt, ctx, qs, tps, s.window, sc.scale, s.dtype,
+                                         rows=range(int(qs[i]), int(qs[i + 1])))
+            else:
+                oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype,
+                                        seqs=[i], sinks=s.sinks)
             kv_bytes += int(2 * (sc.lens[i] - sc.lo[i]) * s.kv_heads * s.head_dim * elt)
             done += 1
     dt = time.perf_counter() - t0
@@ -220,15 +245,26 @@ def main():
                   f"(workload {args.config} has window {base.window})", file=sys.stderr)
             sys.exit(2)
         over = dict(sinks=args.sinks, name=f"{base.name}_sinks{args.sinks}")
+    if args.q_len > 1:
+        base = workloads.config_spec(args.config)
+        over.update(q_lo=args.q_len, q_hi=args.q_len,
+                    name=f"{over.get('name', base.name)}_q{args.q_len}")
     sc = workloads.make_config(args.config, seed=args.seed, device="cuda:0", **over)
     s = sc.spec
     hkv, d = s.kv_heads, s.head_dim
     kv_view = (sc.k_pool, sc.v_pool) if sc.table_page_size == s.page_size else (
         sc.k_pool.view(-1, 1, hkv, d), sc.v_pool.view(-1, 1, hkv, d))
-    out = torch.empty(s.num_seqs, s.q_heads, d, dtype=torch.float32, device=dev)
-    need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
-                                      sc.context_lens, window=s.window, sinks=s.sinks,
-                                      max_context_len=sc.max_context_len)
+    out = torch.empty(len(sc.q), s.q_heads, d, dtype=torch.float32, device=dev)
+    multi = sc.q_start is not None
+    max_q = max(int(sc.nq.max()), 1) if multi else 1
+    if multi:
+        need = ops.prefill_workspace_bytes(sc.q, sc.q_start, kv_view[0], kv_view[1],
+                                           sc.block_tables, sc.context_lens, max_q_len=max_q,
+                                           window=s.window, max_context_len=sc.max_context_len)
+    else:
+        need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
+                                          sc.context_lens, window=s.window, sinks=s.sinks,
+                                          max_context_len=sc.max_context_len)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     flush = None
     if args.flush != "none":
@@ -248,10 +284,14 @@ def main():
         ops.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
 
     def attend():
-        ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
-                   window=s.window, sinks=s.sinks, scale=sc.scale,
-                   max_context_len=sc.max_context_len,
-                   out=out, workspace=ws)
+        if multi:
+            ops.prefill(sc.q, sc.q_start, kv_view[0], kv_view[1], sc.block_tables,
+                        sc.context_lens, max_q_len=max_q, window=s.window, scale=sc.scale,
+                        max_context_len=sc.max_context_len, out=out, workspace=ws)
+        else:
+            ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
+                       window=s.window, sinks=s.sinks, scale=sc.scale,
+                       max_context_len=sc.max_context_len, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -326,6 +366,27 @@ def main():
     dec_avg = float(dec_ms.mean())
     achieved = nb["total"] / (dec_avg * 1e-3) / 1e9
     traffic = measured_traffic(args.traffic, s.name)
+    flops = attention_flops(sc)
+    G = s.q_heads // s.kv_heads
+    streaming = (s.dtype == "bf16" and s.head_dim == 128 and G <= 16 and
+                 (sc.table_page_size & (sc.table_page_size - 1)) == 0 and s.num_seqs <= 2048)
+    if multi:
+        streaming = streaming and (G & (G - 1)) == 0 and s.num_seqs * -(-max_q // (16 // G)) <= 2048
+    call = "pa_prefill" if multi else "pa_decode"
+    kernel = (f"{call} call: decode_stream_kernel (one launch)" if streaming else
+              f"{call} call: per-row kernels and merge")
+    # the bound: matrix cores when the call does more flops per byte than the ridge point
+    if flops / nb["total"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        tflops = flops / (dec_avg * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(tflops, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": flops, "bytes_per_launch": nb["total"]}
+    else:
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "bytes_per_launch": nb["total"], "flops_per_launch": flops}
     result = {
         "metric": "paged decode attention effective KV GB/s (% HBM peak) + seqs/s",
         "value": round(nb["kv"] / (ms_step * 1e-3) / 1e9, 2),
@@ -362,12 +423,12 @@ def main():
                    "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                    "kv_gbps": round(nb["kv"] / (dec_avg * 1e-3) / 1e9, 1),
                    "seqs_per_s": round(s.num_seqs / (dec_avg * 1e-3), 1)},
-        "roofline": {"bound": "hbm",
-                     "kernel": "pa_decode call: decode_stream_kernel (one launch)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": nb["total"]},
+        "roofline": roofline,
     }
+    if multi:
+        result["config"]["q_len"] = max_q
+        result["config"]["num_q"] = int(len(sc.q))
+        result["decode"]["tflops"] = round(flops / (dec_avg * 1e-3) / 1e12, 2)
     if warm is not None:
         result["warm_back_to_back"] = warm
     if s.prefix_len:
