@@ -22,6 +22,8 @@ What it computes, and from which passage:
   mini-sglang page, section on the KV buffer and its store call).
 * ``kvstore.copy_pages`` -- whole-page copy for copy-on-write (silicon chapter
   15, section "The model", ``PageTable.append``).
+* ``tables.update_tables`` -- the per-step scatter of table changes into block
+  and slot tables (the mini-sglang page, section on writing the page table).
 * ``shadow`` -- the page-table semantics as plain per-request row lists, and
   the closed-form page counts of the window rule (silicon chapter 15,
   sections "The problem", "Tests", check 3).
@@ -31,6 +33,6 @@ pages print, closed forms, brute force on tiny inputs, library routines and
 invariances (see ``tests/test_oracle_*.py``).  No function here is parity
 unpinned.
 """
-from . import attention, kvstore, numerics, shadow
+from . import attention, kvstore, numerics, shadow, tables
 
-__all__ = ["attention", "kvstore", "numerics", "shadow"]
+__all__ = ["attention", "kvstore", "numerics", "shadow", "tables"]

@@ -36,6 +36,12 @@ seeds any initial order (a shuffled placement).
 the lifecycle hook of the tiny-llm page "Paged KV Cache" (Task 2), and
 ``pages_needed`` is the page-boundary difference of the mini-sglang page
 (section on paged allocation).
+
+Every change to a request's table (a page mapped, remapped by copy-on-write or
+released) is also recorded as an update ``(request, logical page, physical
+page or -1)``; ``take_table_updates`` hands them over as index lists for one
+device scatter (``pa_update_tables``), the way the mini-sglang page writes new
+table cells with one scatter instead of rebuilding tables on the host.
 """
 from __future__ import annotations
 
@@ -133,6 +139,7 @@ class PagedKVCache:
         self.length: Dict[Hashable, int] = {}
         self.dropped: Dict[Hashable, int] = {}        # pages released by trim
         self.head: Dict[Hashable, int] = {}           # leading pages kept for sink rows
+        self._updates: List[Tuple[Hashable, int, int]] = []   # (request, logical page, page)
 
     # -- lifecycle -------------------------------------------------------------
     def new(self, rid: Hashable, sinks: int = 0) -> None:
@@ -156,6 +163,7 @@ class PagedKVCache:
         if off == 0:
             pages.append(self.pool.alloc())
             new_page = True
+            self._updates.append((rid, row // P, pages[-1]))
         else:
             tail = pages[-1]
             if self.pool.ref[tail] > 1:
@@ -163,6 +171,7 @@ class PagedKVCache:
                 self.pool.unref(tail)
                 pages[-1] = fresh
                 plan_copy = (tail, fresh)
+                self._updates.append((rid, row // P, fresh))
         page = pages[-1]
         self.length[rid] = row + 1
         return AppendPlan(rid, row, page, off, page * P + off, plan_copy, new_page)
@@ -177,6 +186,7 @@ class PagedKVCache:
         while len(pages) > h and (h + self.dropped[rid] + 1) * P <= keep_from:
             p = pages.pop(h)
             self.pool.unref(p)
+            self._updates.append((rid, h + self.dropped[rid], -1))
             self.dropped[rid] += 1
             out.append(p)
         return out
@@ -190,8 +200,11 @@ class PagedKVCache:
         self.head[dst] = self.head[src]
         for p in self.pages[dst]:
             self.pool.incref(p)
+        self._updates.extend((dst, j, p) for j, p in enumerate(self.table(dst)))
 
     def release(self, rid: Hashable) -> None:
+        self._updates.extend((rid, self.logical_page(rid, i), -1)
+                             for i in range(len(self.pages[rid])))
         for p in self.pages.pop(rid):
             self.pool.unref(p)
         del self.length[rid]
@@ -211,6 +224,7 @@ class PagedKVCache:
         pages = self.pages[rid]
         out = []
         while len(pages) > keep:
+            self._updates.append((rid, self.logical_page(rid, len(pages) - 1), -1))
             p = pages.pop()
             self.pool.unref(p)
             out.append(p)
@@ -302,10 +316,29 @@ class PagedKVCache:
         rid = plan.rid
         pages = self.pages[rid]
         self.length[rid] = plan.row
+        j = plan.row // self.page_size
         if plan.new_page:
             self.pool.unref(pages.pop())
+            self._updates.append((rid, j, -1))
         elif plan.copy is not None:
             src, dst = plan.copy
             self.pool.incref(src)
             pages[-1] = src
             self.pool.unref(dst)
+            self._updates.append((rid, j, src))
+
+    def take_table_updates(self, row_of: Dict[Hashable, int]):
+        """The table changes since the last call, as int32 arrays (rows, logical
+        pages, pages) for one scatter: the last change of each cell only, in the
+        order the cells were first changed.  ``row_of`` gives each request's table
+        row; changes of requests it does not name are dropped."""
+        last: Dict[Tuple[int, int], int] = {}
+        for rid, j, p in self._updates:
+            r = row_of.get(rid)
+            if r is not None:
+                last[(r, j)] = p
+        self._updates.clear()
+        cells = list(last)
+        return (np.array([c[0] for c in cells], dtype=np.int32),
+                np.array([c[1] for c in cells], dtype=np.int32),
+                np.array([last[c] for c in cells], dtype=np.int32))

@@ -452,5 +452,54 @@ def pin_prefill():
     return P
 
 
+def pin_tables():
+    """The table scatter: the tiny-llm page's chunk of 6 tokens into pages 7 and 2
+    (page ids [7, 2]; slots of whole pages); and tables kept by scattering the
+    allocator's updates equal the tables it builds, through appends, a fork with
+    copy-on-write, a window trim with sink pages, a rewind and a release."""
+    from paged_kv_cache_41_amd.alloc import PagedKVCache
+    P = []
+    T = oracle.tables
+    bt, st = T.update_tables(np.full((1, 2), -1), np.full((1, 8), 99), [0, 0], [0, 1], [7, 2],
+                             4, 99)
+    if bt.tolist() != [[7, 2]] or st.tolist() != [[28, 29, 30, 31, 8, 9, 10, 11]]:
+        P.append(f"the page's example gives {bt.tolist()} / {st.tolist()}")
+    cache = PagedKVCache(24, 4, free_order=list(range(23, -1, -1)))
+    rows = {"a": 2, "b": 0}
+    bt = np.full((3, 8), -1)
+    st = np.full((3, 32), 96)
+
+    def sync(tag):
+        nonlocal bt, st
+        r, j, p = cache.take_table_updates(rows)
+        bt, st = T.update_tables(bt, st, r, j, p, 4, 96)
+        for rid, row in rows.items():
+            if rid not in cache.pages:
+                if not ((bt[row] == -1).all() and (st[row] == 96).all()):
+                    P.append(f"{tag}: released row {row} not cleared")
+                continue
+            L = cache.length[rid]
+            if bt[row].tolist() != cache.block_tables([rid], 8)[0].tolist():
+                P.append(f"{tag}: block table row of {rid} differs")
+            if st[row, :L].tolist() != cache.slot_table([rid], 32, 96)[0, :L].tolist():
+                P.append(f"{tag}: slot table row of {rid} differs")
+    cache.new("a", sinks=2)
+    for _ in range(10):
+        cache.append("a")
+    sync("appends")
+    cache.fork("a", "b")
+    cache.append("b")                  # copy-on-write of the shared tail page
+    sync("fork")
+    for _ in range(14):
+        cache.append("a")
+    cache.trim("a", 24 + 1 - 6)
+    sync("trim")
+    cache.rewind("b", 3)
+    sync("rewind")
+    cache.release("b")
+    sync("release")
+    return P
+
+
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_window, pin_placement,
-            pin_slot_table, pin_store, pin_copy, pin_sinks, pin_prefill]
+            pin_slot_table, pin_store, pin_copy, pin_sinks, pin_prefill, pin_tables]

@@ -451,3 +451,93 @@ def test_random_operations_with_sinks(seed):
     for rid in list(shadow.rows):
         cache.release(rid)
     assert cache.pool.free_count() == 40 and not any(cache.pool.ref)
+
+
+def _golden_kv(name):
+    return {k: v for k, v in golden(name)}
+
+
+def test_table_updates_prefill_with_pages():
+    """The tiny-llm page's chunk of 6 tokens into pages 7 and 2: the allocator's
+    updates, scattered into empty tables, give the page ids and, in the slot
+    table, whole pages of slots (spare capacity included)."""
+    g = _golden_kv("tinyllm_prefill_with_pages.txt")
+    P, n = int(g["page_size"]), int(g["chunk_tokens"])
+    want = [int(x) for x in g["page_ids"].split()]
+    cache = PagedKVCache(8, P, free_order=want + [p for p in range(8) if p not in want])
+    cache.new("r")
+    for _ in range(n):
+        cache.append("r")
+    assert cache.table("r") == want and cache.length["r"] == int(g["context_len"])
+    rows, js, pages = cache.take_table_updates({"r": 0})
+    assert rows.tolist() == [0, 0] and js.tolist() == [0, 1] and pages.tolist() == want
+    bt, st = oracle.tables.update_tables(np.full((1, 2), -1), np.full((1, 8), 99), rows, js,
+                                         pages, P, 99)
+    assert bt.tolist() == [want]
+    assert st[0].tolist() == [want[0] * P + k for k in range(P)] + [want[1] * P + k for k in range(P)]
+    assert cache.take_table_updates({"r": 0})[0].size == 0          # handed over once
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_table_updates_keep_device_tables_in_step(seed):
+    """Random lifecycles (sinks, forks, copy-on-write, trims, rewinds, releases,
+    rolled-back steps): tables kept only by scattering each round's updates equal
+    the tables rebuilt from the allocator, on every readable row."""
+    R = random.Random(200 + seed)
+    P, NP, ROWS, STRIDE = 4, 48, 6, 40
+    cache = PagedKVCache(NP, P, free_order=R.sample(range(NP), NP))
+    DUMMY = NP * P
+    bt = np.full((ROWS, STRIDE // P), -1)
+    st = np.full((ROWS, STRIDE), DUMMY)
+    row_of, free_rows, nxt = {}, list(range(ROWS)), 0
+    for step in range(300):
+        op = R.choice(["append"] * 5 + ["step", "new", "fork", "trim", "release", "rewind"])
+        ids = list(row_of)
+        try:
+            if op == "new" and free_rows:
+                row_of[nxt] = free_rows.pop(0); cache.new(nxt, sinks=R.choice([0, 0, 3, 6])); nxt += 1
+            elif op == "append" and ids:
+                rid = R.choice(ids)
+                if cache.length[rid] < STRIDE:
+                    cache.append(rid)
+            elif op == "step" and ids:
+                sel = [r for r in ids if cache.length[r] < STRIDE]
+                if sel:
+                    cache.plan_step(sel)
+            elif op == "fork" and ids and free_rows:
+                src = R.choice(ids); row_of[nxt] = free_rows.pop(0); cache.fork(src, nxt); nxt += 1
+            elif op == "trim" and ids:
+                rid = R.choice(ids); cache.trim(rid, R.randrange(0, cache.length[rid] + 1))
+            elif op == "rewind" and ids:
+                rid = R.choice(ids)
+                h, d = cache.head[rid], cache.dropped[rid]
+                floor = (h + d) * P if d else 0
+                cache.rewind(rid, R.randrange(0, max(cache.length[rid] - floor, 0) + 1))
+        except OutOfPages:
+            pass
+        rows, js, pages = cache.take_table_updates(row_of)
+        if op == "release" and ids:
+            rid = R.choice(ids)
+            cache.release(rid)
+            r2, j2, p2 = cache.take_table_updates(row_of)
+            rows, js, pages = (np.concatenate([rows, r2]), np.concatenate([js, j2]),
+                               np.concatenate([pages, p2]))
+            # a cell may appear in both lists: keep the later one
+            seen = {}
+            for i, c in enumerate(zip(rows.tolist(), js.tolist())):
+                seen[c] = i
+            keep = sorted(seen.values())
+            rows, js, pages = rows[keep], js[keep], pages[keep]
+        bt, st = oracle.tables.update_tables(bt, st, rows, js, pages, P, DUMMY)
+        if op == "release" and ids:
+            free_rows.append(row_of.pop(rid))
+        live = list(row_of)
+        if live:
+            ref_bt = cache.block_tables(live, STRIDE // P)
+            ref_st = cache.slot_table(live, STRIDE, dummy_slot=DUMMY)
+            for i, rid in enumerate(live):
+                r, L = row_of[rid], cache.length[rid]
+                assert bt[r].tolist() == ref_bt[i].tolist(), f"seed {seed} op {step} ({op})"
+                assert st[r, :L].tolist() == ref_st[i, :L].tolist(), f"seed {seed} op {step} ({op})"
+        for r in free_rows:
+            assert (bt[r] == -1).all() and (st[r] == DUMMY).all(), f"seed {seed} op {step}: row {r}"

@@ -11,10 +11,12 @@ import oracle
 import pins
 from oracle import attention as A
 from oracle import kvstore as S
+from oracle import tables as TB
 
 _live, _gather, _head, _attend = A.live_rows, A.gather, A.kv_head_of, A.attend
 _rows, _gather_rows = A.attended_rows, A.gather_rows
 _qpos = A.query_position
+_upd = TB.update_tables
 _store, _copy = S.store_kv, S.copy_pages
 
 
@@ -78,6 +80,19 @@ def _gather_rows_first_dup(pool, table_row, rows, dtype):
     return _gather_rows(pool, table_row, rows, dtype)
 
 
+def _upd_release_as_page0(bt, st, rows, js, pages, P, dummy):
+    return _upd(bt, st, rows, js, [max(int(p), 0) for p in pages], P, dummy)
+
+
+def _upd_slot_page_size_one(bt, st, rows, js, pages, P, dummy):
+    # the slot table written as if pages held one row
+    return _upd(bt, None, rows, js, pages, P, dummy)[0], _upd(None, st, rows, js, pages, 1, dummy)[1]
+
+
+def _upd_next_page(bt, st, rows, js, pages, P, dummy):
+    return _upd(bt, st, rows, [int(j) + 1 for j in js], pages, P, dummy)
+
+
 MUTANTS = {
     "gather starts one row late": (A, "live_rows", lambda L, W: (min(_live(L, W)[0] + 1, L), L)),
     "window keeps W+1 rows": (A, "live_rows", lambda L, W: _live(L, W + 1 if W > 0 else 0)),
@@ -101,6 +116,9 @@ MUTANTS = {
     "queries one row late": (A, "query_position", lambda L, n, i: _qpos(L, n, i) + 1),
     "queries one row early": (A, "query_position", lambda L, n, i: _qpos(L, n, i) - 1),
     "every query at the chunk end": (A, "query_position", lambda L, n, i: L - 1),
+    "released cell written as page 0": (TB, "update_tables", _upd_release_as_page0),
+    "slot table written with pages of one row": (TB, "update_tables", _upd_slot_page_size_one),
+    "update lands one page late": (TB, "update_tables", _upd_next_page),
 }
 
 
