@@ -175,6 +175,46 @@ def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
             "gbps_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}
 
 
+def table_update_timing(sc, dev, reps: int = 50) -> dict:
+    """pa_update_tables for one step of this batch: every sequence maps one new page
+    (the page its new row opens), scattered into a copy of the batch's table."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_41_amd import ops
+    s = sc.spec
+    B = s.num_seqs
+    tps = sc.table_page_size
+    table = sc.block_tables.clone()
+    lens = np.maximum(sc.lens, 1)
+    if tps == 1:
+        # slot table: the page's positions get its slots
+        rows = torch.arange(B, dtype=torch.int32, device=dev)
+        js = torch.as_tensor(((lens - 1) // s.page_size).astype(np.int32), device=dev)
+        pages = torch.as_tensor(np.arange(B, dtype=np.int32), device=dev)
+        kw = dict(page_size=s.page_size, slot_table=table, dummy_slot=0)
+    else:
+        rows = torch.arange(B, dtype=torch.int32, device=dev)
+        js = torch.as_tensor(((lens - 1) // tps).astype(np.int32), device=dev)
+        pages = torch.as_tensor(np.arange(B, dtype=np.int32), device=dev)
+        kw = dict(page_size=tps, block_tables=table)
+    f = lambda: ops.update_tables(rows, js, pages, **kw)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    return {"updates": B, "avg_us": round(a.elapsed_time(b) / reps * 1e3, 2),
+            "table": "slot" if tps == 1 else "block",
+            "note": "calls back to back through the Python binding, HIP events on the "
+                    "current stream: the rate the host issues them, an upper bound on the "
+                    "kernel's own time"}
+
+
 def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
     """The oracle, single-threaded, over whole sequences of the batch until ~budget_s."""
     import numpy as np
@@ -433,6 +473,7 @@ def main():
         result["warm_back_to_back"] = warm
     if s.prefix_len:
         result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
+    result["table_update"] = table_update_timing(sc, dev)
     if not args.no_copy_ceiling:
         result["hbm_copy_reference"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:

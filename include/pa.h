@@ -17,7 +17,8 @@
  *                  limited to the last W rows (silicon chapter 15, sections
  *                  "The problem" and "The model"; pa_decode_sinks also keeps
  *                  the first rows, "Exercises"; pa_prefill takes several
- *                  query tokens per sequence; the dense result it must
+ *                  query tokens per sequence; pa_update_tables writes a
+ *                  step's table changes with one scatter; the dense result it must
  *                  equal is the checkpoint of the tiny-llm page "Paged KV
  *                  Cache", section "Correctness Checkpoint").
  *
@@ -184,6 +185,30 @@ int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_
                int32_t num_pages, int32_t page_size, int32_t window, int32_t max_context_len,
                float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
                void* stream);
+
+/*
+ * pa_update_tables -- one step's table changes as one scatter (the mini-sglang
+ * page, part 4, section on writing the page table: new cells are written with
+ * one indexed store from host-built index lists, not request by request).
+ *   block_tables  device int32 [bt_rows, bt_stride], or NULL: cell
+ *                 [rows[i], logical_pages[i]] = pages[i] (pages[i] < 0: -1).
+ *   slot_table    device int32 [slot_rows, slot_stride], or NULL: positions
+ *                 logical_pages[i] * page_size + k, k < page_size, of row
+ *                 rows[i] = pages[i] * page_size + k, or dummy_slot when
+ *                 pages[i] < 0 (a whole page of positions, spare capacity
+ *                 included, as that page's token expansion writes them).
+ *   rows, logical_pages, pages  device int32 [num_updates].
+ *   An update outside a table (row, column or position) is skipped for that
+ *   table.  Two updates of one cell in one call are a caller error (either
+ *   value may remain).  Ownership: every pointer is caller-owned device memory.
+ *   Errors: PA_EINVAL for num_updates < 0, page_size <= 0, a non-positive
+ *   stride of a table that is passed, or missing index lists.
+ */
+int pa_update_tables(int32_t* block_tables, int32_t bt_stride, int32_t bt_rows,
+                     int32_t* slot_table, int32_t slot_stride, int32_t slot_rows,
+                     int32_t dummy_slot, const int32_t* rows, const int32_t* logical_pages,
+                     const int32_t* pages, int32_t num_updates, int32_t page_size,
+                     void* stream);
 
 #ifdef __cplusplus
 }

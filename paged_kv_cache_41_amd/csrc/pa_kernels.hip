@@ -322,6 +322,27 @@ inline int launch_rows(const DecodeArgs& a, DecodeFn generic, bool fast, int hea
   return PA_OK;
 }
 
+// Table updates: update i maps logical page logical[i] of table row rows[i] to page
+// pages[i] (-1: released) in the block table, and its page_size positions to the page's
+// slots (or the dummy slot) in the slot table.  Cells outside a table are skipped.
+__global__ __launch_bounds__(64) void update_tables_kernel(
+    int32_t* __restrict__ bt, int bt_stride, int bt_rows, int32_t* __restrict__ st,
+    int st_stride, int st_rows, int dummy_slot, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ logical, const int32_t* __restrict__ pages, int n, int P) {
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int r = rows[i], j = logical[i], p = pages[i];
+    if (bt && threadIdx.x == 0 && r >= 0 && r < bt_rows && j >= 0 && j < bt_stride)
+      bt[(size_t)r * bt_stride + j] = p >= 0 ? p : -1;
+    if (st && r >= 0 && r < st_rows && j >= 0) {
+      for (int k = threadIdx.x; k < P; k += 64) {
+        const int64_t pos = (int64_t)j * P + k;
+        if (pos < st_stride)
+          st[(size_t)r * st_stride + pos] = p >= 0 ? (int32_t)((int64_t)p * P + k) : dummy_slot;
+      }
+    }
+  }
+}
+
 // Query row r of a prefill chunk as a row of its own: its sequence (the last s with
 // q_start[s] <= r) and its context, position + 1 (0 when it lies before row 0 or outside
 // its sequence's rows).
@@ -650,4 +671,22 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + rows_bytes);
   a.ws_acc = a.ws_ml + 2 * parts;
   return launch_rows(a, generic, fast, head_dim, st);
+}
+
+extern "C" int pa_update_tables(int32_t* block_tables, int32_t bt_stride, int32_t bt_rows,
+                                int32_t* slot_table, int32_t slot_stride, int32_t slot_rows,
+                                int32_t dummy_slot, const int32_t* rows,
+                                const int32_t* logical_pages, const int32_t* pages,
+                                int32_t num_updates, int32_t page_size, void* stream) {
+  if (num_updates < 0 || page_size <= 0) return PA_EINVAL;
+  if (block_tables && (bt_stride <= 0 || bt_rows < 0)) return PA_EINVAL;
+  if (slot_table && (slot_stride <= 0 || slot_rows < 0)) return PA_EINVAL;
+  if (num_updates == 0 || (!block_tables && !slot_table)) return PA_OK;
+  if (!rows || !logical_pages || !pages) return PA_EINVAL;
+  const int grid = num_updates < 65535 ? num_updates : 65535;
+  hipLaunchKernelGGL(update_tables_kernel, dim3(grid), dim3(64), 0,
+                     reinterpret_cast<hipStream_t>(stream), block_tables, bt_stride, bt_rows,
+                     slot_table, slot_stride, slot_rows, dummy_slot, rows, logical_pages, pages,
+                     num_updates, page_size);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }

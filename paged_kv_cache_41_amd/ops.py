@@ -206,3 +206,35 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
                   scale, max_context_len, workspace.data_ptr(),
                   workspace.numel() * workspace.element_size(), _stream(dev, stream))
     return out
+
+
+def update_tables(rows, logical_pages, pages, *, page_size: int,
+                  block_tables: Optional[torch.Tensor] = None,
+                  slot_table: Optional[torch.Tensor] = None, dummy_slot: int = 0,
+                  stream=None) -> None:
+    """Scatter one step's table changes (``pa_update_tables``) into the tables, in place.
+
+    ``rows``, ``logical_pages``, ``pages``: int32 ``[n]`` on the device (for instance
+    ``PagedKVCache.take_table_updates`` moved there); ``pages[i] < 0`` releases the cell.
+    """
+    tabs = [t for t in (block_tables, slot_table) if t is not None]
+    dev = _dev(rows, logical_pages, pages, *tabs)
+    for name, t in (("rows", rows), ("logical_pages", logical_pages), ("pages", pages)):
+        _i32(t, name)
+    n = int(rows.numel())
+    if logical_pages.numel() != n or pages.numel() != n:
+        raise ValueError("index lists differ in length")
+    for name, t in (("block_tables", block_tables), ("slot_table", slot_table)):
+        if t is not None:
+            _i32(t, name)
+            if t.dim() != 2:
+                raise ValueError(f"{name} must be 2-D")
+    bt = block_tables
+    st = slot_table
+    lib = _lib.load()
+    _lib.check("pa_update_tables", lib.pa_update_tables(
+        bt.data_ptr() if bt is not None else None, int(bt.shape[1]) if bt is not None else 0,
+        int(bt.shape[0]) if bt is not None else 0,
+        st.data_ptr() if st is not None else None, int(st.shape[1]) if st is not None else 0,
+        int(st.shape[0]) if st is not None else 0, int(dummy_slot), rows.data_ptr(),
+        logical_pages.data_ptr(), pages.data_ptr(), n, int(page_size), _stream(dev, stream)))

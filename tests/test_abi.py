@@ -85,6 +85,13 @@ def test_argument_validation_needs_no_gpu():
     assert pre(4, 5, 0, 32, 8, 128, 1) == _lib.PA_EINVAL
     assert pre(4, 32, 8, 32, 8, 128, 1) == _lib.PA_OK and size.value > 0
     assert pre(4, 32, 8, 32, 8, 64, 0) == _lib.PA_OK and size.value > 0
+    # table updates: nothing to do, or invalid sizes, never touch a device
+    fake = ctypes.c_void_p(256)
+    assert lib.pa_update_tables(None, 0, 0, None, 0, 0, 0, None, None, None, 0, 4, None) == _lib.PA_OK
+    assert lib.pa_update_tables(fake, 8, 4, None, 0, 0, 0, None, None, None, -1, 4, None) == _lib.PA_EINVAL
+    assert lib.pa_update_tables(fake, 8, 4, None, 0, 0, 0, fake, fake, fake, 3, 0, None) == _lib.PA_EINVAL
+    assert lib.pa_update_tables(fake, 0, 4, None, 0, 0, 0, fake, fake, fake, 3, 4, None) == _lib.PA_EINVAL
+    assert lib.pa_update_tables(fake, 8, 4, None, 0, 0, 0, None, fake, fake, 3, 4, None) == _lib.PA_EINVAL
     # store / copy: bad dtype, zero-sized no-ops
     assert lib.pa_store_kv(None, None, None, None, None, 1, 8, 16, 8, 128, 7, None) == _lib.PA_EINVAL
     assert lib.pa_store_kv(None, None, None, None, None, 0, 8, 16, 8, 128, 1, None) == _lib.PA_OK
