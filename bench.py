@@ -175,6 +175,30 @@ def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
             "gbps_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}
 
 
+def memory_report(sc) -> dict:
+    """Pages the batch holds and their fragmentation: unused slots of each sequence's
+    final page over the slots of its live pages (host arithmetic on the tables)."""
+    import numpy as np
+    s = sc.spec
+    P = s.page_size
+    bt = sc.block_tables.cpu().numpy()
+    live = unused = 0
+    for i in range(s.num_seqs):
+        L = int(sc.lens[i])
+        if L == 0:
+            continue
+        if sc.table_page_size == 1:
+            n = len({int(x) // P for x in bt[i, :L]} & set(range(sc.pool_pages)))
+        else:
+            n = int((bt[i] >= 0).sum())
+        live += n * P
+        unused += (-L) % P
+    row_bytes = 2 * s.kv_heads * s.head_dim * (4 if s.dtype == "f32" else 2)
+    return {"live_page_slots": live, "unused_last_page_slots": unused,
+            "fragmentation": round(unused / live, 5) if live else 0.0,
+            "unused_bytes": unused * row_bytes, "pool_pages": sc.pool_pages}
+
+
 def table_update_timing(sc, dev, reps: int = 50) -> dict:
     """pa_update_tables for one step of this batch: every sequence maps one new page
     (the page its new row opens), scattered into a copy of the batch's table."""
@@ -474,6 +498,7 @@ def main():
     if s.prefix_len:
         result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
     result["table_update"] = table_update_timing(sc, dev)
+    result["memory"] = memory_report(sc)
     if not args.no_copy_ceiling:
         result["hbm_copy_reference"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:
