@@ -70,6 +70,10 @@ constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
 #ifndef STREAM_DEPTH
 #define STREAM_DEPTH 2   // tiles of K/V in flight per wavefront while one is computed
 #endif
+#ifndef STREAM_MULTI_DEPTH
+#define STREAM_MULTI_DEPTH 1   // the same with several query tokens per sequence (its
+                               // registers go to the query groups)
+#endif
 
 struct Tile {
   uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
@@ -284,22 +288,28 @@ struct Front {
   }
 };
 
-template <int DEPTH, bool PAGE_TILES, bool MULTI>
+// NB = 0: one query token per sequence.  NB > 0 (MULTI): several query tokens per
+// sequence, taken in groups of NB blocks of 16 / G tokens; a group's NB x 16 score
+// columns share every K/V tile a wavefront loads.
+template <int DEPTH, bool PAGE_TILES, int NB>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
+  constexpr bool MULTI = NB > 0;
+  constexpr int NBX = MULTI ? NB : 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int Hkv = a.kv_heads;
   const int G = a.group;
-  // score columns in use: the G heads, or (MULTI) 16 / G query tokens of G heads each
-  const int C = MULTI ? 16 : G;
+  // score columns in use: the G heads, or (MULTI) NB x 16 / G query tokens of G heads each;
+  // column c is then head c % G of the group's query token c / G
+  const int C = MULTI ? 16 * NB : G;
   const int lg = MULTI ? 31 - __clz(G) : 0;   // G is a power of two with MULTI
-  int B = a.num_seqs;                         // segments per kv head: sequences or blocks
+  int B = a.num_seqs;                         // segments per kv head: sequences or groups
 
   if constexpr (MULTI) {
-    // ---- blocks of 16 / G query tokens: counts per sequence, prefix sum, block records,
-    // then tile counts per block and their prefix sum ----------------------------------
-    const int tpb = 16 >> lg;
+    // ---- groups of NB x 16 / G query tokens: counts per sequence, prefix sum, group
+    // records, then tile counts per group and their prefix sum -------------------------
+    const int tpb = (16 >> lg) * NB;
     for (int s = tid; s < B; s += 64 * NW) {
       const int q0 = a.q_start[s];
       int n = a.q_start[s + 1] - q0;
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     __syncthreads();
     wg_exclusive_scan(st_cum, VB, tid, lane, w);
     B = VB;
-    // query rows of blocks with nothing to attend are zero
+    // query rows of groups with nothing to attend are zero
     for (int v = blockIdx.x; v < B; v += gridDim.x) {
       if (st_cum[v + 1] != st_cum[v]) continue;
       float* out = a.out + (size_t)st_q0[v] * a.q_heads * HD;
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   auto load_tile = [&](const Desc& d, int e, Tile& Tl) {
     const int t0 = d.t0;
-    if (d.flags & (RANGE_FIRST | SEG_FIRST)) {
+    if (NB <= 1 && (d.flags & (RANGE_FIRST | SEG_FIRST))) {
       // the query rows of the group, fetched with the tile so that waiting for them is
       // waiting for this tile; lanes past the group read head 0 and are zeroed later
       size_t qr;
@@ -509,15 +519,26 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // m_ref: reference max of score column col (query head col), the same in every lane
   // group; l_run: this lane's share of the running sum (its four tokens); oacc[e][r]:
   // output of query head 4 grp + r at column 8 col + e.
-  bf16x8 qb[4];
-  float m_ref = -INFINITY, l_run = 0.f;
-  f32x4 oacc[8];
+  // One set per block of 16 columns (decode: one).
+  bf16x8 qb[NBX][4];
+  float m_ref[NBX], l_run[NBX];
+  f32x4 oacc[NBX][8];
   bool first_seg = true;     // the segment being computed is the first of the range
   bool started_here = false; // ... and its tile 0 lies in this range
-  // this lane's score column is in use; (MULTI) the rows its query may attend are
-  // (pc_lo, pc]
-  bool cval = col < G;
-  int pc = 0, pc_lo = 0;
+  // this lane's score column of each block is in use; (MULTI) the rows its query may
+  // attend are (pc_lo, pc]
+  bool cval[NBX];
+  int pc[NBX], pc_lo[NBX];
+  // (MULTI) a tile of rows [t0, t0 + 16) with t0 + 15 <= seg_pmin and t0 > seg_plo is
+  // attended by every query of the segment's group
+  int seg_pmin = 0, seg_plo = 0;
+#pragma unroll
+  for (int i = 0; i < NBX; ++i) {
+    m_ref[i] = -INFINITY;
+    l_run[i] = 0.f;
+    cval[i] = col < G;
+    pc[i] = pc_lo[i] = 0;
+  }
   // partial area: the (max, sum) pair of every slot and column, then their accumulators
   const uint32_t nslots = (uint32_t)a.total_waves * 2 * C;
   const DevBuf part(a.ws_ml, nslots * (2 + HD) * 4);
@@ -531,60 +552,91 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   auto begin_segment = [&](const Desc& d, const Tile& Tl) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
     if constexpr (MULTI) {
-      cval = (col >> lg) < st_nt[d.s];
-      pc = st_p0[d.s] + (col >> lg);
-      pc_lo = a.window > 0 ? pc - a.window : (-0x7fffffff - 1);
+      const int nt = st_nt[d.s], p0 = st_p0[d.s], q0 = st_q0[d.s];
+      seg_pmin = uni(p0);
+      seg_plo = uni(a.window > 0 ? p0 + nt - 1 - a.window : (-0x7fffffff - 1));
+#pragma unroll
+      for (int i = 0; i < NBX; ++i) {
+        const int tq = ((i * 16 + col) >> lg);   // query token of this lane's column
+        cval[i] = tq < nt;
+        pc[i] = p0 + tq;
+        pc_lo[i] = a.window > 0 ? pc[i] - a.window : (-0x7fffffff - 1);
+        if constexpr (NB > 1) {
+          // the group's queries, read here (a wait for them drains the loads in flight,
+          // once per segment)
+          const uint4* qrow = reinterpret_cast<const uint4*>(
+              reinterpret_cast<const uint16_t*>(a.q) +
+              ((size_t)(q0 + (cval[i] ? tq : 0)) * a.q_heads + (size_t)d.g * G +
+               (col & (G - 1))) * HD + grp * 32);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qb[i][j] = as_bf16x8(cval[i] ? qrow[j] : zero);
+        }
+      }
+    }
+    if constexpr (NB <= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qb[0][j] = as_bf16x8(cval[0] ? Tl.q[j] : zero);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(cval ? Tl.q[j] : zero);
-    m_ref = -INFINITY;
-    l_run = 0.f;
+    for (int i = 0; i < NBX; ++i) {
+      m_ref[i] = -INFINITY;
+      l_run[i] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) oacc[i][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     started_here = (d.flags & SEG_FIRST) != 0;
   };
 
   auto end_segment = [&](const Desc& d, bool complete) {
-    float lt = l_run;
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    float lr[4];
+    float* out = a.out + ((size_t)d.s * a.q_heads + (size_t)d.g * G) * HD + col * 8;
+    int ncols = G;
+    if constexpr (MULTI) {
+      out = a.out + ((size_t)st_q0[d.s] * a.q_heads + (size_t)d.g * G) * HD + col * 8;
+      ncols = st_nt[d.s] << lg;
+    }
+    // a piece of a segment cut by a range boundary: partial (max, sum, accumulator) to
+    // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
+    // through to the point where every compute unit reads it)
+    const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lr[r] = __shfl(lt, 4 * grp + r, 64);
-    if (complete) {
-      float* out = a.out + ((size_t)d.s * a.q_heads + (size_t)d.g * G) * HD + col * 8;
-      int ncols = G;
-      if constexpr (MULTI) {
-        out = a.out + ((size_t)st_q0[d.s] * a.q_heads + (size_t)d.g * G) * HD + col * 8;
-        ncols = st_nt[d.s] << lg;
-      }
+    for (int i = 0; i < NBX; ++i) {
+      float lt = l_run[i];
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      float lr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        if (h < ncols) {
-          const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;
-          // MULTI: column h is head h % G of query token h / G (rows q_heads apart)
-          const size_t row = MULTI ? (size_t)(h >> lg) * a.q_heads + (h & (G - 1)) : (size_t)h;
-          float4* o = reinterpret_cast<float4*>(out + row * HD);
-          o[0] = make_float4(oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv);
-          o[1] = make_float4(oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv);
+      for (int r = 0; r < 4; ++r) lr[r] = __shfl(lt, 4 * grp + r, 64);
+      if (complete) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = i * 16 + 4 * grp + r;
+          if (h < ncols) {
+            const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;
+            // MULTI: column h is head h % G of query token h / G (rows q_heads apart)
+            const size_t row = MULTI ? (size_t)(h >> lg) * a.q_heads + (h & (G - 1)) : (size_t)h;
+            float4* o = reinterpret_cast<float4*>(out + row * HD);
+            const f32x4* ac = oacc[i];
+            o[0] = make_float4(ac[0][r] * inv, ac[1][r] * inv, ac[2][r] * inv, ac[3][r] * inv);
+            o[1] = make_float4(ac[4][r] * inv, ac[5][r] * inv, ac[6][r] * inv, ac[7][r] * inv);
+          }
+        }
+      } else {
+        const int c0 = i * 16;
+        if (lane < min(C - c0, 16))
+          part.store2(ml_off((uint32_t)(pi * C + c0 + lane)), make_float2(m_ref[i], lt));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = c0 + 4 * grp + r;
+          if (h < C) {
+            const uint32_t o = acc_off((uint32_t)(pi * C + h)) + col * 32;
+            const f32x4* ac = oacc[i];
+            part.store4(o, make_float4(ac[0][r], ac[1][r], ac[2][r], ac[3][r]));
+            part.store4(o + 16, make_float4(ac[4][r], ac[5][r], ac[6][r], ac[7][r]));
+          }
         }
       }
-    } else {
-      // a piece of a segment cut by a range boundary: partial (max, sum, accumulator) to
-      // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
-      // through to the point where every compute unit reads it)
-      const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
-      if (lane < C) part.store2(ml_off((uint32_t)pi * C + lane), make_float2(m_ref, lt));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        if (h < C) {
-          const uint32_t o = acc_off((uint32_t)pi * C + h) + col * 32;
-          part.store4(o, make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]));
-          part.store4(o + 16, make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]));
-        }
-      }
+    }
+    if (!complete) {
       const int tiles = st_cum[d.s + 1] - st_cum[d.s];
       const int seg_start = Hkv * st_cum[d.s] + d.g * tiles;
       const int k1 = range_of(T, R, seg_start), k2 = range_of(T, R, seg_start + tiles - 1);
@@ -605,54 +657,74 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   auto compute = [&](const Tile& Tl, const Desc& d) {
     if (d.flags & (RANGE_FIRST | SEG_FIRST)) begin_segment(d, Tl);
-    // scores S[token][head] = K . q
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // scores S[token][column] = K . q, one product per block of 16 columns
+    f32x4 sc[NBX];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[j]), qb[j], sc, 0, 0, 0);
-    float sv[4];
-    float mt = -INFINITY;
+    for (int i = 0; i < NBX; ++i) {
+      sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bool ok = (Tl.valid >> (4 * grp + r)) & 1;
-      if constexpr (MULTI) {
-        const int t = d.t0 + 4 * grp + r;
-        ok = ok && t <= pc && t > pc_lo;
-      }
-      sv[r] = ok ? sc[r] * a.qscale : -INFINITY;
-      mt = fmaxf(mt, sv[r]);
+      for (int j = 0; j < 4; ++j)
+        sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[j]), qb[i][j], sc[i], 0, 0,
+                                                        0);
     }
-    // raise the reference when some head's tile max passes it by more than RESCALE_T;
-    // this lane's own max decides whether any does, so the cross-lane max is only taken
-    // on the (rare) raise
-    if (__ballot(cval && mt > m_ref + RESCALE_T) != 0) {
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m_ref, mt);
-      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
-      l_run *= alpha;
-      m_ref = mn;
+    // a tile whose rows every column attends needs no masks (most tiles of long contexts)
+    bool plain = Tl.valid == 0xffffull;
+    if constexpr (MULTI) plain = plain && d.t0 + 15 <= seg_pmin && d.t0 > seg_plo;
+    bf16x4 phi[NBX], plo[NBX];
+#pragma unroll
+    for (int i = 0; i < NBX; ++i) {
+      float sv[4];
+      float mt = -INFINITY;
+      if (plain) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = sc[i][r] * a.qscale;
+          mt = fmaxf(mt, sv[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bool ok = (Tl.valid >> (4 * grp + r)) & 1;
+          if constexpr (MULTI) {
+            const int t = d.t0 + 4 * grp + r;
+            ok = ok && t <= pc[i] && t > pc_lo[i];
+          }
+          sv[r] = ok ? sc[i][r] * a.qscale : -INFINITY;
+          mt = fmaxf(mt, sv[r]);
+        }
+      }
+      // raise the reference when some column's tile max passes it by more than RESCALE_T;
+      // this lane's own max decides whether any does, so the cross-lane max is only taken
+      // on the (rare) raise
+      if (__ballot(cval[i] && mt > m_ref[i] + RESCALE_T) != 0) {
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m_ref[i], mt);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[i] - mn);
+        l_run[i] *= alpha;
+        m_ref[i] = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oacc[i][e][r] *= ar;
+        }
+      }
+      const float ms = m_ref[i] == -INFINITY ? 0.f : m_ref[i];
+      float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * grp + r, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[e][r] *= ar;
+        p[r] = cval[i] ? __builtin_amdgcn_exp2f(sv[r] - ms) : 0.f;
+        l_run[i] += p[r];
       }
+      // P as the A operand (row = column col, k = token 4 grp + r), split into a bf16 high
+      // part and the bf16-rounded remainder
+      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+      const uint32_t l01 = pack_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+      phi[i] = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
+      plo[i] = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
     }
-    const float ms = m_ref == -INFINITY ? 0.f : m_ref;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = cval ? __builtin_amdgcn_exp2f(sv[r] - ms) : 0.f;
-      l_run += p[r];
-    }
-    // P as the A operand (row = head col, k = token 4 grp + r), split into a bf16 high
-    // part and the bf16-rounded remainder
-    const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
-    const uint32_t l01 = pack_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-    const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-    const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
-    const bf16x4 plo = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
     // Rows outside the attended range get probability 0, but their V may be anything
     // (rows of the last page past the sequence end are never written): replace them by
     // zeros, since 0 * NaN would poison the product.
@@ -668,13 +740,17 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // column 8 col + e of the four tokens: the B operand (k = token, n = column block)
+      // column 8 col + e of the four tokens: the B operand (k = token, n = column block),
+      // gathered once and used by every block
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
       const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
       const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
-      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, oacc[e], 0, 0, 0);
-      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, oacc[e], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NBX; ++i) {
+        oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[i], bv, oacc[i][e], 0, 0, 0);
+        oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[i], bv, oacc[i][e], 0, 0, 0);
+      }
     }
     if (d.flags & (SEG_LAST | RANGE_LAST))
       end_segment(d, (d.flags & SEG_LAST) && started_here);
@@ -812,22 +888,29 @@ inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_
          tiles_bound(num_seqs, kv_heads, max_live, sinks) < ((int64_t)1 << 30);
 }
 
-// Several query tokens per sequence: blocks of 16 / group tokens, each attending at most
-// `keys` rows (the window plus the block's other tokens, or the whole context).
-inline int64_t blocks_bound(int num_seqs, int group, int max_q) {
-  const int tpb = 16 / group;
-  return (int64_t)num_seqs * ((max_q + tpb - 1) / tpb);
+// Several query tokens per sequence: groups of nb blocks of 16 / group tokens, each
+// attending at most `keys` rows (the window plus the group's other tokens, or the whole
+// context).  Longer chunks take more blocks per group, so that more query columns share
+// every K/V tile.
+inline int multi_blocks(int group, int max_q) {
+  // four blocks (64 columns) would need more registers than a wavefront has
+  return max_q <= 16 / group ? 1 : 2;
 }
-inline int64_t tiles_bound_multi(int num_seqs, int kv_heads, int group, int max_q, int keys) {
-  return blocks_bound(num_seqs, group, max_q) * kv_heads * ((keys + 15) / 16 + 1);
+inline int64_t blocks_bound(int num_seqs, int group, int max_q, int nb) {
+  const int tpg = 16 / group * nb;
+  return (int64_t)num_seqs * ((max_q + tpg - 1) / tpg);
+}
+inline int64_t tiles_bound_multi(int num_seqs, int kv_heads, int group, int max_q, int keys,
+                                 int nb) {
+  return blocks_bound(num_seqs, group, max_q, nb) * kv_heads * ((keys + 15) / 16 + 1);
 }
 inline bool eligible_multi(int dtype, int head_dim, int group, int page_size, int num_seqs,
-                           int bt_stride, int kv_heads, int max_q, int keys) {
+                           int bt_stride, int kv_heads, int max_q, int keys, int nb) {
   return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
          (group & (group - 1)) == 0 && page_size > 0 && (page_size & (page_size - 1)) == 0 &&
-         num_seqs >= 1 && max_q >= 1 && blocks_bound(num_seqs, group, max_q) <= BMAX &&
+         num_seqs >= 1 && max_q >= 1 && blocks_bound(num_seqs, group, max_q, nb) <= BMAX &&
          (int64_t)num_seqs * bt_stride < ((int64_t)1 << 31) &&
-         tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys) < ((int64_t)1 << 30);
+         tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys, nb) < ((int64_t)1 << 30);
 }
 
 // Workspace: the arrival counters (zero between calls), then per wavefront two partial
@@ -846,19 +929,23 @@ inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
   a.ws_acc = a.ws_ml + slots * 2;
 }
 
-inline int launch(const DecodeArgs& a, hipStream_t st, bool multi) {
-  const unsigned blocks = (unsigned)(a.total_waves / NW);
-  const dim3 grid(blocks), block(64 * NW);
-  if (multi) {
-    if (a.page_size >= TILE)
-      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false, true>), grid, block, 0, st, a);
-  } else {
-    if (a.page_size >= TILE)
-      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, true, false>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_stream_kernel<STREAM_DEPTH, false, false>), grid, block, 0, st, a);
+template <int NB>
+inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
+  constexpr int D = NB > 0 ? STREAM_MULTI_DEPTH : STREAM_DEPTH;
+  if (a.page_size >= TILE)
+    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB>), grid, block, 0, st, a);
+}
+
+// nb = 0: one query token per sequence; 1 or 2: blocks per group of query tokens
+inline int launch(const DecodeArgs& a, hipStream_t st, int nb) {
+  const dim3 grid((unsigned)(a.total_waves / NW)), block(64 * NW);
+  switch (nb) {
+    case 0: launch_nb<0>(a, st, grid, block); break;
+    case 1: launch_nb<1>(a, st, grid, block); break;
+    case 2: launch_nb<2>(a, st, grid, block); break;
+    default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -507,8 +507,8 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
     a.qscale = scale * 1.4426950408889634f;
     a.total_waves = (int)waves;
     stream::carve_workspace(a, workspace, group);
-    return stream::launch(a, reinterpret_cast<hipStream_t>(stream), false) == 0 ? PA_OK
-                                                                               : PA_ELAUNCH;
+    return stream::launch(a, reinterpret_cast<hipStream_t>(stream), 0) == 0 ? PA_OK
+                                                                           : PA_ELAUNCH;
   }
   a.chunk = pick_chunk(max_live);
   const bool fast = mfma::eligible(dtype, head_dim, group, page_size);
@@ -608,19 +608,20 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   a.qscale = scale * 1.4426950408889634f;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  // keys one block of 16 / group query tokens may attend
-  const int tpb = 16 / group;
-  const int64_t keys64 = window > 0 ? (int64_t)window + tpb - 1 : (int64_t)max_context_len;
+  // keys one group of query tokens may attend
+  const int nb = (group & (group - 1)) == 0 ? stream::multi_blocks(group, max_q) : 1;
+  const int tpg = 16 / group * nb;
+  const int64_t keys64 = window > 0 ? (int64_t)window + tpg - 1 : (int64_t)max_context_len;
   const int keys = (int)(keys64 < max_context_len ? keys64 : max_context_len);
   if (stream::eligible_multi(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
-                             max_q, keys)) {
+                             max_q, keys, nb)) {
     const int64_t tiles_max =
-        stream::tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys);
+        stream::tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys, nb);
     int64_t waves = tiles_max / 22;
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
-    const size_t need = stream::workspace_bytes((int)waves, 16);
+    const size_t need = stream::workspace_bytes((int)waves, 16 * nb);
     if (!workspace) {
       *workspace_bytes = need;
       return PA_OK;
@@ -638,8 +639,8 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
     a.num_q = num_q;
     a.max_q = max_q;
     a.total_waves = (int)waves;
-    stream::carve_workspace(a, workspace, 16);
-    return stream::launch(a, st, true) == 0 ? PA_OK : PA_ELAUNCH;
+    stream::carve_workspace(a, workspace, 16 * nb);
+    return stream::launch(a, st, nb) == 0 ? PA_OK : PA_ELAUNCH;
   }
 
   // every query row as a row of its own: its sequence and context first, then the rows path
