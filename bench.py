@@ -439,6 +439,12 @@ def main():
     call = "pa_prefill" if multi else "pa_decode"
     kernel = (f"{call} call: decode_stream_kernel (one launch)" if streaming else
               f"{call} call: per-row kernels and merge")
+    if multi:
+        tiles = s.num_seqs * s.kv_heads * -(-max_q // (64 // G)) if (G & (G - 1)) == 0 else 0
+        if (s.dtype == "bf16" and s.head_dim == 128 and G <= 16 and (G & (G - 1)) == 0 and
+                (sc.table_page_size & (sc.table_page_size - 1)) == 0 and max_q * G >= 128 and
+                tiles >= 1024):
+            kernel = "pa_prefill call: prefill_tile_kernel (one launch)"
     # the bound: matrix cores when the call does more flops per byte than the ridge point
     if flops / nb["total"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         tflops = flops / (dec_avg * 1e-3) / 1e12

@@ -25,6 +25,7 @@
 #include "pa_common.hpp"
 #include "pa_decode_mfma.hpp"
 #include "pa_decode_stream.hpp"
+#include "pa_prefill_tile.hpp"
 
 namespace pa {
 
@@ -607,6 +608,24 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   a.max_ctx = max_context_len;
   a.qscale = scale * 1.4426950408889634f;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  // long chunks: a workgroup per tile of 64 query columns, K/V shared through LDS
+  if (ptile::eligible(dtype, head_dim, group, page_size, num_seqs, kv_heads, max_q)) {
+    if (!workspace) {
+      *workspace_bytes = 0;
+      return PA_OK;
+    }
+    if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens)
+      return PA_EINVAL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+      return PA_EUNSUPPORTED;
+    a.ctx = context_lens;
+    a.num_seqs = num_seqs;
+    a.q_start = q_start;
+    a.num_q = num_q;
+    a.max_q = max_q;
+    return ptile::launch(a, st) == 0 ? PA_OK : PA_ELAUNCH;
+  }
 
   // keys one group of query tokens may attend
   const int nb = (group & (group - 1)) == 0 ? stream::multi_blocks(group, max_q) : 1;

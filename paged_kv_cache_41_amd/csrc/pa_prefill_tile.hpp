@@ -1,0 +1,305 @@
+// Prefill chunks: several query tokens per sequence, many of them (bf16 pools, head_dim
+// 128, G = q_heads / kv_heads a power of two up to 16, page sizes that are powers of two).
+//
+// One workgroup of four wavefronts per (sequence, kv head, tile of 64 score columns); a
+// column is one query head of one query token (column c: head c % G of token c / G of the
+// tile), so a tile holds 64 / G query tokens.  Wavefront w takes columns 16 w .. 16 w + 15.
+// The workgroup walks the key rows its tile's queries attend, from the window start of
+// its first query to its last query's own row, 64 rows at a time: the K and V rows of the
+// next 64 are loaded by all 256 lanes (each lane 64 bytes of K and of V) while the current
+// ones are computed, and written to one of two LDS buffers, so every K/V byte is read from
+// memory once per tile and shared by its 64 columns.  Each wavefront reads the keys and
+// values from LDS in the matrix-core operand layouts of the decode kernels: scores with
+// v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 of head_dim, B = the 16 columns' queries),
+// base-2 online softmax with a lazily raised reference max, P.V with
+// v_mfma_f32_16x16x16_bf16 (P as bf16 high part plus bf16 remainder, V gathered with
+// v_perm_b32).  Each column is masked to its own query's rows (causal, the window counted
+// from its row); a 64-row block that every column attends skips the masks.  A workgroup
+// covers its tile's whole key range, so there is no split and nothing to merge; every key
+// row loaded lies in [window start of the first query, last query's row], which are rows
+// some query attends, so every table entry read is a mapped page.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_common.hpp"
+#include "pa_decode_mfma.hpp"
+
+namespace pa {
+namespace ptile {
+
+using mfma::as_bf16x8;
+using mfma::bf16x8;
+using mfma::f32x4;
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int HD = 128;
+constexpr int KT = 64;            // key rows per block
+constexpr int COLS = 64;          // score columns per workgroup
+constexpr int ROWB = 256 + 16;    // LDS bytes per key row (one kv head's 256 bytes, padded)
+constexpr float RESCALE_T = 8.f;
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2v h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int lg = 31 - __clz(G);
+  const int Hkv = a.kv_heads;
+  const int tpt = COLS >> lg;                       // query tokens per tile
+  const int QT = (a.max_q + tpt - 1) / tpt;         // tiles per sequence at most
+  const int qt = blockIdx.x % QT;
+  const int sg = blockIdx.x / QT;
+  const int g = sg % Hkv;
+  const int s = sg / Hkv;
+
+  // the sequence's query rows, clamped to the bounds the host passed
+  const int q0 = a.q_start[s];
+  int n = a.q_start[s + 1] - q0;
+  if (q0 < 0 || q0 > a.num_q) n = 0;
+  n = max(0, min(min(n, a.num_q - q0), a.max_q));
+  const int tk0 = qt * tpt;
+  if (tk0 >= n) return;                             // uniform over the workgroup
+  const int nt = min(tpt, n - tk0);
+  const int ctx = a.ctx[s];
+  const int L = ctx > 0 ? (ctx < a.max_ctx ? ctx : a.max_ctx) : 0;
+  const int p0 = L - n + tk0;                       // row of the tile's first query
+  const int kend = max(p0 + nt, 0);                 // one past its last query's row
+  const int lo = a.window > 0 ? max(p0 + 1 - a.window, 0) : 0;
+  float* out = a.out + ((size_t)(q0 + tk0) * a.q_heads + (size_t)g * G) * HD;
+  if (kend <= lo) {
+    // every query of the tile lies before row 0: zero rows
+    for (int i = tid; i < nt * G * HD; i += 256) {
+      const int t = i / (G * HD), r = i - t * G * HD;
+      out[(size_t)t * a.q_heads * HD + r] = 0.f;
+    }
+    return;
+  }
+
+  // this lane's column: head (c & (G - 1)) of query token c >> lg of the tile
+  const int c = w * 16 + col;
+  const int tq = c >> lg;
+  const bool cval = tq < nt;
+  const int pc = p0 + tq;
+  const int pc_lo = a.window > 0 ? pc - a.window : (-0x7fffffff - 1);
+  // a block of rows [k0, k0 + 64) with k0 + 63 <= pmin and k0 > plo is attended by all
+  const int pmin = p0;
+  const int plo = a.window > 0 ? p0 + nt - 1 - a.window : (-0x7fffffff - 1);
+
+  bf16x8 qb[4];
+  {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.q) +
+        ((size_t)(q0 + tk0 + (cval ? tq : 0)) * a.q_heads + (size_t)g * G + (c & (G - 1))) * HD +
+        grp * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(cval ? qrow[j] : zero);
+  }
+
+  const int P = a.page_size;
+  const int lp = 31 - __clz(P);
+  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
+  const uint32_t page_bytes = row_bytes * (uint32_t)P;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * HD * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * HD * 2;
+  const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
+  const int last_page = a.num_pages - 1;
+
+  // loading: lane tid takes key row kk = tid / 4 of the block, bytes [64 part, +64)
+  const int kk = tid >> 2, part = tid & 3;
+  const int kt0 = lo & ~(KT - 1);
+  const int nblk = (kend - 1 - kt0) / KT + 1;
+  // (the key of block b is written out in each lambda: a lambda that calls another one
+  // keeps its closure in scratch memory)
+  auto entry = [&](int b) __attribute__((always_inline)) { return btr[min(max(kt0 + b * KT + kk, lo), kend - 1) >> lp]; };
+  // (the rows travel in named registers: arrays or structs shared between the lambdas
+  // and the loop stayed in scratch memory)
+  uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
+  auto load = [&](int b, int e) __attribute__((always_inline)) {
+    const int key = min(max(kt0 + b * KT + kk, lo), kend - 1);
+    const int pg = min(max(e, 0), last_page);
+    const size_t off = (size_t)(uint32_t)pg * page_bytes + (size_t)(key & (P - 1)) * row_bytes +
+                       part * 64;
+    const uint4* kp = reinterpret_cast<const uint4*>(kbase + off);
+    const uint4* vp = reinterpret_cast<const uint4*>(vbase + off);
+    rk0 = kp[0];
+    rk1 = kp[1];
+    rk2 = kp[2];
+    rk3 = kp[3];
+    rv0 = vp[0];
+    rv1 = vp[1];
+    rv2 = vp[2];
+    rv3 = vp[3];
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+    uint4* kd = reinterpret_cast<uint4*>(&lds_k[buf][kk * ROWB + part * 64]);
+    uint4* vd = reinterpret_cast<uint4*>(&lds_v[buf][kk * ROWB + part * 64]);
+    kd[0] = rk0;
+    kd[1] = rk1;
+    kd[2] = rk2;
+    kd[3] = rk3;
+    vd[0] = rv0;
+    vd[1] = rv1;
+    vd[2] = rv2;
+    vd[3] = rv3;
+  };
+
+  float m_ref = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int b, int buf) __attribute__((always_inline)) {
+    const int k0 = kt0 + b * KT;
+    const char* Ks = lds_k[buf];
+    const char* Vs = lds_v[buf];
+    // scores of the 64 rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* kr = Ks + (kb * 16 + col) * ROWB + grp * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * j)), qb[j], sc[kb], 0, 0, 0);
+    }
+    float sv[4][4];
+    float mt = -INFINITY;
+    const bool plain = k0 + KT - 1 <= pmin && k0 > plo;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = k0 + kb * 16 + 4 * grp + r;
+        const bool ok = plain || (t <= pc && t > pc_lo);
+        sv[kb][r] = ok ? sc[kb][r] * a.qscale : -INFINITY;
+        mt = fmaxf(mt, sv[kb][r]);
+      }
+    if (__ballot(cval && mt > m_ref + RESCALE_T) != 0) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+      l_run *= alpha;
+      m_ref = mn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[e][r] *= ar;
+      }
+    }
+    const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = cval ? __builtin_amdgcn_exp2f(sv[kb][r] - ms) : 0.f;
+        l_run += p[r];
+      }
+      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+      const uint32_t l01 = pack_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+      const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
+      const bf16x4 plo_ = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
+      // V rows 16 kb + 4 grp + j, bytes [16 col, +16): the B operand gathered by v_perm
+      uint4 vt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vt[j] = *reinterpret_cast<const uint4*>(Vs + (kb * 16 + 4 * grp + j) * ROWB + col * 16);
+      const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
+      const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
+      const uint32_t v2[4] = {vt[2].x, vt[2].y, vt[2].z, vt[2].w};
+      const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+        const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
+        const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo_, bv, oacc[e], 0, 0, 0);
+      }
+    }
+  };
+
+  // pipeline: block b computed from LDS while block b + 1 is loaded into registers, then
+  // written to the other buffer; the table entry is read one block further ahead
+  // (past the last block the loads repeat it: in range, and never staged)
+  const int bl = nblk - 1;
+  load(0, entry(0));
+  int e1 = entry(min(1, bl));
+  stage(0);
+  load(min(1, bl), e1);
+  int e2 = entry(min(2, bl));
+  __syncthreads();
+  for (int b = 0; b < nblk; ++b) {
+    compute(b, b & 1);
+    if (b + 1 < nblk) {
+      stage((b + 1) & 1);
+      load(min(b + 2, bl), e2);
+      e2 = entry(min(b + 3, bl));
+    }
+    __syncthreads();
+  }
+
+  // output: lane (col, grp) holds columns 4 grp + r of its wavefront at head_dim 8 col + e
+  float lt = l_run;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lr = __shfl(lt, 4 * grp + r, 64);
+    const int h = w * 16 + 4 * grp + r;
+    if ((h >> lg) < nt) {
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      float4* o = reinterpret_cast<float4*>(
+          out + ((size_t)(h >> lg) * a.q_heads + (h & (G - 1))) * HD + col * 8);
+      o[0] = make_float4(oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv);
+      o[1] = make_float4(oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv);
+    }
+  }
+}
+
+// Tiles per sequence at most and the grid; the path serves chunks of at least two tiles'
+// worth of query columns with enough workgroups to cover the chip.
+inline int64_t grid_size(int num_seqs, int kv_heads, int group, int max_q) {
+  const int tpt = COLS / group;
+  return (int64_t)num_seqs * kv_heads * ((max_q + tpt - 1) / tpt);
+}
+inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs,
+                     int kv_heads, int max_q) {
+  return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
+         (group & (group - 1)) == 0 && page_size > 0 && (page_size & (page_size - 1)) == 0 &&
+         num_seqs >= 1 && (int64_t)max_q * group >= 2 * COLS &&
+         grid_size(num_seqs, kv_heads, group, max_q) >= 1024 &&
+         grid_size(num_seqs, kv_heads, group, max_q) < ((int64_t)1 << 31);
+}
+
+inline int launch(const DecodeArgs& a, hipStream_t st) {
+  const int64_t blocks = grid_size(a.num_seqs, a.kv_heads, a.group, a.max_q);
+  hipLaunchKernelGGL(prefill_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace ptile
+}  // namespace pa

@@ -210,6 +210,36 @@ MULTI = {
 }
 
 
+# Long chunks over enough (sequence, kv head, 64-column) tiles: the tile kernel with K/V
+# staged through LDS.
+MULTI_TILE = {
+    "tile_g4_p16": dict(_GQA, num_seqs=16, page_size=16, len_lo=130, len_hi=700, q_lo=60,
+                        q_hi=130, spare="nan"),
+    "tile_g4_p16_w100": dict(_GQA, num_seqs=16, page_size=16, window=100, len_lo=130,
+                             len_hi=700, q_lo=60, q_hi=130),
+    "tile_g4_p4_w37": dict(_GQA, num_seqs=16, page_size=4, window=37, len_lo=100, len_hi=500,
+                           q_lo=70, q_hi=130, spare="nan"),
+    "tile_g1_p8": dict(dtype="bf16", q_heads=8, kv_heads=8, head_dim=128, num_seqs=48,
+                       page_size=8, len_lo=100, len_hi=400, q_lo=65, q_hi=140),
+    "tile_g16_p32": dict(dtype="bf16", q_heads=32, kv_heads=2, head_dim=128, num_seqs=24,
+                         page_size=32, len_lo=40, len_hi=300, q_lo=10, q_hi=130),
+    "tile_g8_slots": dict(dtype="bf16", q_heads=64, kv_heads=8, head_dim=128, num_seqs=8,
+                          page_size=16, len_lo=40, len_hi=400, q_lo=20, q_hi=140,
+                          slot_table=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_TILE))
+def test_prefill_tile(name):
+    sc = workloads.build(workloads.Spec(name=f"prefill_{name}", pool_factor=1.25,
+                                        **MULTI_TILE[name]), 47, device="cuda")
+    s = sc.spec
+    G = s.q_heads // s.kv_heads
+    tiles = s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (64 // G))
+    assert tiles >= 1024 and int(sc.nq.max()) * G >= 128    # the tile path's conditions
+    check_step(sc)
+
+
 @pytest.mark.parametrize("name", sorted(MULTI))
 def test_prefill(name):
     sc = workloads.build(workloads.Spec(name=f"prefill_{name}", pool_factor=1.25,
@@ -231,16 +261,18 @@ def test_prefill_many_blocks_rows_path():
 
 def test_prefill_more_queries_than_rows():
     # contexts shortened below the chunk length: queries before row 0 give zero rows
-    spec = workloads.Spec(name="prefill_short", **_GQA, num_seqs=12, page_size=16, len_lo=1,
+    spec = workloads.Spec(name="prefill_short", **_GQA, num_seqs=24, page_size=16, len_lo=1,
                           len_hi=120, q_lo=4, q_hi=24, pool_factor=1.25)
     sc = workloads.build(spec, 43, device="cuda")
     o = ops()
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
     ctx = sc.context_lens.clone()
     ctx[::2] = torch.as_tensor(sc.nq[::2] // 2, device="cuda", dtype=torch.int32)
-    for path in ("stream", "rows"):
-        # the rows path through fp32 would need other pools: force it with a larger bound
-        mq = max(int(sc.nq.max()), 1) if path == "stream" else 2048
+    assert int(sc.nq.max()) * 4 < 128 and len(sc.q) >= 170
+    for path in ("stream", "tile"):
+        # the bound on query tokens picks the path: the shape's own bound (under 32 tokens)
+        # streams; 170 makes 24 x 8 x 11 tiles of 16 tokens, enough for the tile kernel
+        mq = {"stream": max(int(sc.nq.max()), 1), "tile": 170}[path]
         out = o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, ctx,
                         max_q_len=mq, scale=sc.scale).cpu().double().numpy()
         ref = oracle.attention.prefill(bits(sc.q), bits(sc.k_pool), bits(sc.v_pool),
