@@ -40,7 +40,21 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 constexpr int HD = 128;
 constexpr int KT = 64;            // key rows per block
 constexpr int COLS = 64;          // score columns per workgroup
-constexpr int ROWB = 256 + 16;    // LDS bytes per key row (one kv head's 256 bytes, padded)
+#ifndef PTILE_ROWB
+#define PTILE_ROWB (256 + 16)
+#endif
+#ifndef PTILE_DIE_MAJOR
+#define PTILE_DIE_MAJOR 1
+#endif
+constexpr int ROWB = PTILE_ROWB;  // LDS bytes per key row (one kv head's 256 bytes, padded)
+#ifndef PTILE_SWZ
+#define PTILE_SWZ 0
+#endif
+// byte offset of 16-byte chunk `ch` (0..15) of key row `row` in an LDS buffer; the chunk
+// index may be XOR-swizzled by the row
+__device__ __forceinline__ int lds_off(int row, int ch) {
+  return row * ROWB + ((ch ^ (row & PTILE_SWZ)) << 4);
+}
 constexpr float RESCALE_T = 8.f;
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -64,8 +78,18 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
   const int Hkv = a.kv_heads;
   const int tpt = COLS >> lg;                       // query tokens per tile
   const int QT = (a.max_q + tpt - 1) / tpt;         // tiles per sequence at most
-  const int qt = blockIdx.x % QT;
-  const int sg = blockIdx.x / QT;
+  // Workgroups go to the eight dies round-robin (workgroup b to die b % 8); numbering the
+  // work die-major gives each die a contiguous run of it, so the query tiles of one
+  // (sequence, kv head), which read the same key rows, share that die's L2.
+  int wid = blockIdx.x;
+#if PTILE_DIE_MAJOR
+  {
+    const int nb = gridDim.x, x = wid & 7, i = wid >> 3, q = nb >> 3, r = nb & 7;
+    wid = x * q + min(x, r) + i;
+  }
+#endif
+  const int qt = wid % QT;
+  const int sg = wid / QT;
   const int g = sg % Hkv;
   const int s = sg / Hkv;
 
@@ -149,16 +173,16 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     rv3 = vp[3];
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
-    uint4* kd = reinterpret_cast<uint4*>(&lds_k[buf][kk * ROWB + part * 64]);
-    uint4* vd = reinterpret_cast<uint4*>(&lds_v[buf][kk * ROWB + part * 64]);
-    kd[0] = rk0;
-    kd[1] = rk1;
-    kd[2] = rk2;
-    kd[3] = rk3;
-    vd[0] = rv0;
-    vd[1] = rv1;
-    vd[2] = rv2;
-    vd[3] = rv3;
+    char* kd = lds_k[buf];
+    char* vd = lds_v[buf];
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 0)) = rk0;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 1)) = rk1;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 2)) = rk2;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 3)) = rk3;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 0)) = rv0;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 1)) = rv1;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 2)) = rv2;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 3)) = rv3;
   };
 
   float m_ref = -INFINITY, l_run = 0.f;
@@ -170,29 +194,53 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     const int k0 = kt0 + b * KT;
     const char* Ks = lds_k[buf];
     const char* Vs = lds_v[buf];
-    // scores of the 64 rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col
+    // scores of the 64 rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col.
+    // All sixteen K fragments are read first, so their LDS latency overlaps.
+    uint4 kf[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kf[kb][j] = *reinterpret_cast<const uint4*>(Ks + lds_off(kb * 16 + col, 4 * grp + j));
     f32x4 sc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const char* kr = Ks + (kb * 16 + col) * ROWB + grp * 64;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * j)), qb[j], sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][j]), qb[j], sc[kb], 0,
+                                                         0, 0);
     }
-    float sv[4][4];
-    float mt = -INFINITY;
-    const bool plain = k0 + KT - 1 <= pmin && k0 > plo;
+    // V rows 16 kb + 4 grp + j, bytes [16 col, +16), read now: in flight during the softmax
+    uint4 vf[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = k0 + kb * 16 + 4 * grp + r;
-        const bool ok = plain || (t <= pc && t > pc_lo);
-        sv[kb][r] = ok ? sc[kb][r] * a.qscale : -INFINITY;
-        mt = fmaxf(mt, sv[kb][r]);
-      }
+      for (int j = 0; j < 4; ++j)
+        vf[kb][j] = *reinterpret_cast<const uint4*>(Vs + lds_off(kb * 16 + 4 * grp + j, col));
+    float sv[4][4];
+    float mt = -INFINITY;
+    // a block every column attends takes no masks (a uniform branch); in the others each
+    // score is kept or set to -inf with a select, not a branch
+    if (k0 + KT - 1 <= pmin && k0 > plo) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[kb][r] = sc[kb][r] * a.qscale;
+          mt = fmaxf(mt, sv[kb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = k0 + kb * 16 + 4 * grp + r;
+          const bool ok = (t <= pc) & (t > pc_lo);
+          sv[kb][r] = ok ? sc[kb][r] * a.qscale : -INFINITY;
+          mt = fmaxf(mt, sv[kb][r]);
+        }
+    }
     if (__ballot(cval && mt > m_ref + RESCALE_T) != 0) {
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
@@ -221,15 +269,11 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
       const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
       const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
       const bf16x4 plo_ = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
-      // V rows 16 kb + 4 grp + j, bytes [16 col, +16): the B operand gathered by v_perm
-      uint4 vt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vt[j] = *reinterpret_cast<const uint4*>(Vs + (kb * 16 + 4 * grp + j) * ROWB + col * 16);
-      const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
-      const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
-      const uint32_t v2[4] = {vt[2].x, vt[2].y, vt[2].z, vt[2].w};
-      const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
+      // the B operand of column block col gathered from the four rows by v_perm
+      const uint32_t v0[4] = {vf[kb][0].x, vf[kb][0].y, vf[kb][0].z, vf[kb][0].w};
+      const uint32_t v1[4] = {vf[kb][1].x, vf[kb][1].y, vf[kb][1].z, vf[kb][1].w};
+      const uint32_t v2[4] = {vf[kb][2].x, vf[kb][2].y, vf[kb][2].z, vf[kb][2].w};
+      const uint32_t v3[4] = {vf[kb][3].x, vf[kb][3].y, vf[kb][3].z, vf[kb][3].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
