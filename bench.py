@@ -124,15 +124,20 @@ def unique_kv_bytes(sc) -> int:
     return len(seen) * rows_per * 2 * s.kv_heads * s.head_dim * elt
 
 
+# The files the decode call's kernel is compiled from, and its build flags.
+DECODE_SOURCES = ("paged_kv_cache_41_amd/csrc/pa_decode_stream.hpp",
+                  "paged_kv_cache_41_amd/csrc/pa_common.hpp",
+                  "paged_kv_cache_41_amd/csrc/pa_decode_mfma.hpp",
+                  "include/pa.h", "paged_kv_cache_41_amd/build.py")
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of the HIP sources the library is built from (names and contents)."""
-    import glob
+    """Hash of the decode kernel's sources (names and contents)."""
     import hashlib
-    csrc = os.path.join(ROOT, "paged_kv_cache_41_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+    for f in DECODE_SOURCES:
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()
 
 
