@@ -818,8 +818,14 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
   const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
   if (!last0 && !last1) return;
-  // One wavefront combines a segment: lane l takes columns 4 (l % 32) .. +3 of heads
-  // l / 32, l / 32 + 2, ...; the partials of COMBINE_BATCH pieces are loaded together.
+  // One wavefront combines a segment, CPP columns per pass: lane l takes head_dim
+  // (128 / CPP) ... of column l / (64 / CPP) (+ CPP per pass); the partials of
+  // COMBINE_BATCH pieces are loaded together.  Decode (at most 16 columns, usually a few)
+  // takes 4 columns per pass, several query tokens (16 or 32 columns) 8, which needs more
+  // registers.
+  constexpr int CPP = MULTI ? 8 : 4;
+  constexpr int LPC = 64 / CPP;             // lanes per column
+  constexpr int QPL = HD / LPC / 4;         // float4 per lane
   auto combine = [&](int seg, int k1, int k2) {
     const int s = seg / Hkv, g = seg % Hkv;
     const int tiles = st_cum[s + 1] - st_cum[s];
@@ -832,19 +838,23 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       out = a.out + ((size_t)st_q0[s] * a.q_heads + (size_t)g * G) * HD;
       ncols = st_nt[s] << lg;
     }
-    const int c4 = (lane & 31) * 4;
-    for (int h = lane >> 5; h < ncols; h += 2) {
+    const int cd = (lane % LPC) * (QPL * 4);
+    for (int h = lane / LPC; h < ncols; h += CPP) {
       float M = -INFINITY, den = 0.f;
-      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 nm[QPL];
+#pragma unroll
+      for (int q = 0; q < QPL; ++q) nm[q] = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int k0 = k1; k0 <= k2; k0 += COMBINE_BATCH) {
         float2 ml[COMBINE_BATCH];
-        float4 x[COMBINE_BATCH];
+        float4 x[COMBINE_BATCH][QPL];
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
           const size_t pi = (size_t)k * 2 + (k == k1 ? slot1 : 0);
           ml[b] = part.load2(ml_off((uint32_t)pi * C + h));
-          x[b] = part.load4(acc_off((uint32_t)pi * C + h) + c4 * 4);
+          const uint32_t o = acc_off((uint32_t)pi * C + h) + cd * 4;
+#pragma unroll
+          for (int q = 0; q < QPL; ++q) x[b][q] = part.load4(o + 16 * q);
         }
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
@@ -853,17 +863,22 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
           const float mn = fmaxf(M, mm);
           const float fo = exp2f(M - mn), fn = exp2f(mm - mn);
           den = den * fo + ml[b].y * fn;
-          num.x = num.x * fo + x[b].x * fn;
-          num.y = num.y * fo + x[b].y * fn;
-          num.z = num.z * fo + x[b].z * fn;
-          num.w = num.w * fo + x[b].w * fn;
+#pragma unroll
+          for (int q = 0; q < QPL; ++q) {
+            nm[q].x = nm[q].x * fo + x[b][q].x * fn;
+            nm[q].y = nm[q].y * fo + x[b][q].y * fn;
+            nm[q].z = nm[q].z * fo + x[b][q].z * fn;
+            nm[q].w = nm[q].w * fo + x[b][q].w * fn;
+          }
           M = mn;
         }
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
       const size_t row = MULTI ? (size_t)(h >> lg) * a.q_heads + (h & (G - 1)) : (size_t)h;
-      *reinterpret_cast<float4*>(out + row * HD + c4) =
-          make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+      float4* o = reinterpret_cast<float4*>(out + row * HD + cd);
+#pragma unroll
+      for (int q = 0; q < QPL; ++q)
+        o[q] = make_float4(nm[q].x * inv, nm[q].y * inv, nm[q].z * inv, nm[q].w * inv);
     }
     if (lane == 0)
       __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
