@@ -326,6 +326,10 @@ EDGE = {
     "nan_spare_p1": dict(q_heads=8, kv_heads=2, head_dim=128, page_size=1, len_lo=0, len_hi=300, spare="nan"),
     "nan_spare_p64": dict(q_heads=16, kv_heads=4, head_dim=128, page_size=64, window=70, len_lo=1, len_hi=700, spare="nan"),
     "nan_spare_generic_f32": dict(q_heads=4, kv_heads=2, head_dim=64, dtype="f32", page_size=4, window=5, len_lo=1, len_hi=90, spare="nan"),
+    "all_empty": dict(num_seqs=3, q_heads=8, kv_heads=2, head_dim=128, lens=(0, 0, 0)),
+    # one sequence across the whole grid: every segment is cut into dozens of pieces
+    "one_seq_20k": dict(num_seqs=1, q_heads=32, kv_heads=8, head_dim=128, lens=(20000,)),
+    "one_seq_20k_g16": dict(num_seqs=1, q_heads=16, kv_heads=1, head_dim=128, lens=(20000,)),
 }
 
 
@@ -592,3 +596,72 @@ def test_decode_loop_device_tables():
         for r, L in zip(rids, ctx):
             cache.trim(r, int(L) + 1 - (W - S))
     assert 5 in cache.pages and cache.length[5] == 30
+
+
+def test_batch_at_streaming_limit():
+    # exactly as many sequences as the streaming path takes
+    spec = workloads.Spec(name="b2048", dtype="bf16", num_seqs=2048, q_heads=8, kv_heads=2,
+                          head_dim=128, page_size=16, len_lo=0, len_hi=64, pool_factor=1.25)
+    sc = workloads.build(spec, 19, device="cuda")
+    rng = np.random.default_rng(5)
+    seqs = sorted(set(rng.choice(2048, 40, replace=False).tolist()) | {0, 2047})
+    check_step(sc, seqs=seqs)
+
+
+def test_graph_replays_match_eager():
+    """The step (table scatter, copy, store, decode; and a verify step through pa_prefill)
+    captured in a HIP graph and replayed several times, with eager work and
+    synchronizations in between: every replay equals the eager result bit for bit.  The
+    workspaces are zero-filled once before capture; the calls put their counters back to
+    zero themselves, so no memset is recorded."""
+    o = ops()
+    sc = workloads.make_config(2, device="cuda")
+    s = sc.spec
+    B = s.num_seqs
+    ws = torch.zeros(o.decode_workspace_bytes(sc.q, sc.k_pool, sc.v_pool, sc.block_tables,
+                                              sc.context_lens, max_context_len=sc.max_context_len),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, s.q_heads, s.head_dim, device="cuda")
+    # a table update that rewrites each sequence's last page with itself (same values)
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    js = torch.as_tensor(((np.maximum(sc.lens, 1) - 1) // 16).astype(np.int32), device="cuda")
+    pages = sc.block_tables[rows.long(), js.long()].contiguous()
+    k0, v0 = sc.k_pool.clone(), sc.v_pool.clone()
+    qv = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    outv = torch.empty_like(out)
+    wsv = torch.zeros(max(o.prefill_workspace_bytes(sc.q, qv, sc.k_pool, sc.v_pool,
+                                                    sc.block_tables, sc.context_lens,
+                                                    max_q_len=1), 1),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        o.update_tables(rows, js, pages, page_size=16, block_tables=sc.block_tables)
+        o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
+        o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+        o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens, scale=sc.scale,
+                 max_context_len=sc.max_context_len, out=out, workspace=ws)
+        o.prefill(sc.q, qv, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens, max_q_len=1,
+                  scale=sc.scale, out=outv, workspace=wsv)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()                                   # eager, on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    want, wantv = out.clone(), outv.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))
+        outv.fill_(float("nan"))
+        sc.k_pool.copy_(k0)                      # eager work between the replays
+        sc.v_pool.copy_(v0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {i}: decode differs from the eager call"
+        assert torch.equal(outv, wantv), f"replay {i}: verify step differs from the eager call"
+    assert not torch.isnan(want).any()
+    assert (ws[:4096] == 0).all(), "the arrival counters must be back at zero"
