@@ -5,16 +5,17 @@
 // column is one query head of one query token (column c: head c % G of token c / G of the
 // tile), so a tile holds 64 / G query tokens.  Wavefront w takes columns 16 w .. 16 w + 15.
 // The workgroup walks the key rows its tile's queries attend, from the window start of
-// its first query to its last query's own row, 64 rows at a time: the K and V rows of the
-// next 64 are loaded by all 256 lanes (each lane 64 bytes of K and of V) while the current
+// its first query to its last query's own row, 32 rows at a time: the K and V rows of the
+// next 32 are loaded by all 256 lanes (each lane 32 bytes of K and of V) while the current
 // ones are computed, and written to one of two LDS buffers, so every K/V byte is read from
-// memory once per tile and shared by its 64 columns.  Each wavefront reads the keys and
-// values from LDS in the matrix-core operand layouts of the decode kernels: scores with
-// v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 of head_dim, B = the 16 columns' queries),
-// base-2 online softmax with a lazily raised reference max, P.V with
-// v_mfma_f32_16x16x16_bf16 (P as bf16 high part plus bf16 remainder, V gathered with
-// v_perm_b32).  Each column is masked to its own query's rows (causal, the window counted
-// from its row); a 64-row block that every column attends skips the masks.  A workgroup
+// memory once per tile and shared by its 64 columns.  Blocks of 32 rows (rather than 64)
+// leave registers and LDS for three workgroups per compute unit.  Each wavefront reads the keys and
+// values from LDS in matrix-core operand layouts: scores with v_mfma_f32_16x16x32_bf16
+// (A = 16 keys x 32 of head_dim, B = the 16 columns' queries), base-2 online softmax with
+// a lazily raised reference max, P.V with v_mfma_f32_16x16x16_bf16 (P as bf16 high part
+// plus bf16 remainder; the V operand read with transposing LDS reads, ds_read_b64_tr_b16,
+// which hand each lane one head_dim column of four key rows).  Each column is masked to its own query's rows (causal, the window counted
+// from its row); a block that every column attends skips the masks.  A workgroup
 // covers its tile's whole key range, so there is no split and nothing to merge; every key
 // row loaded lies in [window start of the first query, last query's row], which are rows
 // some query attends, so every table entry read is a mapped page.
@@ -38,23 +39,26 @@ typedef short bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 128;
-constexpr int KT = 64;            // key rows per block
+#ifndef PTILE_KT
+#define PTILE_KT 32
+#endif
+constexpr int KT = PTILE_KT;      // key rows per block
+constexpr int NKB = KT / 16;      // blocks of 16 rows in a matrix-core product
+constexpr int TPR = 256 / KT;     // lanes loading one key row
+constexpr int UPT = KT / 16;      // 16-byte pieces of K (and of V) each lane loads
+#ifndef PTILE_WG_PER_CU
+#define PTILE_WG_PER_CU 3
+#endif
 constexpr int COLS = 64;          // score columns per workgroup
 #ifndef PTILE_ROWB
-#define PTILE_ROWB (256 + 16)
+#define PTILE_ROWB (256 + 32)
 #endif
 #ifndef PTILE_DIE_MAJOR
 #define PTILE_DIE_MAJOR 1
 #endif
 constexpr int ROWB = PTILE_ROWB;  // LDS bytes per key row (one kv head's 256 bytes, padded)
-#ifndef PTILE_SWZ
-#define PTILE_SWZ 0
-#endif
-// byte offset of 16-byte chunk `ch` (0..15) of key row `row` in an LDS buffer; the chunk
-// index may be XOR-swizzled by the row
-__device__ __forceinline__ int lds_off(int row, int ch) {
-  return row * ROWB + ((ch ^ (row & PTILE_SWZ)) << 4);
-}
+// byte offset of 16-byte chunk `ch` (0..15) of key row `row` in an LDS buffer
+__device__ __forceinline__ int lds_off(int row, int ch) { return row * ROWB + (ch << 4); }
 constexpr float RESCALE_T = 8.f;
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -64,7 +68,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-__global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
   __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
 
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
   const bool cval = tq < nt;
   const int pc = p0 + tq;
   const int pc_lo = a.window > 0 ? pc - a.window : (-0x7fffffff - 1);
-  // a block of rows [k0, k0 + 64) with k0 + 63 <= pmin and k0 > plo is attended by all
+  // a block of rows [k0, k0 + KT) with k0 + KT - 1 <= pmin and k0 > plo is attended by all
   const int pmin = p0;
   const int plo = a.window > 0 ? p0 + nt - 1 - a.window : (-0x7fffffff - 1);
 
@@ -146,8 +150,9 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
   const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
   const int last_page = a.num_pages - 1;
 
-  // loading: lane tid takes key row kk = tid / 4 of the block, bytes [64 part, +64)
-  const int kk = tid >> 2, part = tid & 3;
+  // loading: lane tid takes key row kk = tid / TPR of the block, 16-byte pieces
+  // UPT part .. UPT part + UPT - 1 of it
+  const int kk = tid / TPR, part = tid % TPR;
   const int kt0 = lo & ~(KT - 1);
   const int nblk = (kend - 1 - kt0) / KT + 1;
   // (the key of block b is written out in each lambda: a lambda that calls another one
@@ -160,29 +165,34 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     const int key = min(max(kt0 + b * KT + kk, lo), kend - 1);
     const int pg = min(max(e, 0), last_page);
     const size_t off = (size_t)(uint32_t)pg * page_bytes + (size_t)(key & (P - 1)) * row_bytes +
-                       part * 64;
+                       part * UPT * 16;
     const uint4* kp = reinterpret_cast<const uint4*>(kbase + off);
     const uint4* vp = reinterpret_cast<const uint4*>(vbase + off);
     rk0 = kp[0];
     rk1 = kp[1];
-    rk2 = kp[2];
-    rk3 = kp[3];
     rv0 = vp[0];
     rv1 = vp[1];
-    rv2 = vp[2];
-    rv3 = vp[3];
+    if constexpr (UPT > 2) {
+      rk2 = kp[2];
+      rk3 = kp[3];
+      rv2 = vp[2];
+      rv3 = vp[3];
+    }
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
     char* kd = lds_k[buf];
     char* vd = lds_v[buf];
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 0)) = rk0;
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 1)) = rk1;
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 2)) = rk2;
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, 4 * part + 3)) = rk3;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 0)) = rv0;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 1)) = rv1;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 2)) = rv2;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, 4 * part + 3)) = rv3;
+    const int c0 = part * UPT;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 0)) = rk0;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 1)) = rk1;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 0)) = rv0;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 1)) = rv1;
+    if constexpr (UPT > 2) {
+      *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 2)) = rk2;
+      *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 3)) = rk3;
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 2)) = rv2;
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 3)) = rv3;
+    }
   };
 
   float m_ref = -INFINITY, l_run = 0.f;
@@ -194,37 +204,42 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     const int k0 = kt0 + b * KT;
     const char* Ks = lds_k[buf];
     const char* Vs = lds_v[buf];
-    // scores of the 64 rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col.
-    // All sixteen K fragments are read first, so their LDS latency overlaps.
-    uint4 kf[4][4];
+    // scores of the block's rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col.
+    // All K fragments of the block are read first, so their LDS latency overlaps.
+    uint4 kf[NKB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         kf[kb][j] = *reinterpret_cast<const uint4*>(Ks + lds_off(kb * 16 + col, 4 * grp + j));
-    f32x4 sc[4];
+    f32x4 sc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][j]), qb[j], sc[kb], 0,
                                                          0, 0);
     }
-    // V rows 16 kb + 4 grp + j, bytes [16 col, +16), read now: in flight during the softmax
-    uint4 vf[4][4];
+    // The P.V operand of head_dim 16 e .. 16 e + 15, read now (in flight during the
+    // softmax) with transposing LDS reads: in each group of 16 lanes, lane L reads 4
+    // consecutive values of key row 4 grp + L / 4 at head_dim 16 e + 4 (L % 4), and the read
+    // hands lane L the values of its head_dim 16 e + L from the group's four key rows.
+    bf16x4 vb[NKB][8];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vf[kb][j] = *reinterpret_cast<const uint4*>(Vs + lds_off(kb * 16 + 4 * grp + j, col));
-    float sv[4][4];
+      for (int e = 0; e < 8; ++e)
+        vb[kb][e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) bf16x4*)(Vs + (kb * 16 + 4 * grp + (col >> 2)) * ROWB +
+                                                        32 * e + 8 * (col & 3)));
+    float sv[NKB][4];
     float mt = -INFINITY;
     // a block every column attends takes no masks (a uniform branch); in the others each
     // score is kept or set to -inf with a select, not a branch
     if (k0 + KT - 1 <= pmin && k0 > plo) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sv[kb][r] = sc[kb][r] * a.qscale;
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
         }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = k0 + kb * 16 + 4 * grp + r;
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     }
     const float ms = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -269,19 +284,10 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
       const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
       const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
       const bf16x4 plo_ = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
-      // the B operand of column block col gathered from the four rows by v_perm
-      const uint32_t v0[4] = {vf[kb][0].x, vf[kb][0].y, vf[kb][0].z, vf[kb][0].w};
-      const uint32_t v1[4] = {vf[kb][1].x, vf[kb][1].y, vf[kb][1].z, vf[kb][1].w};
-      const uint32_t v2[4] = {vf[kb][2].x, vf[kb][2].y, vf[kb][2].z, vf[kb][2].w};
-      const uint32_t v3[4] = {vf[kb][3].x, vf[kb][3].y, vf[kb][3].z, vf[kb][3].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
-        const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
-        const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo_, bv, oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb[kb][e], oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo_, vb[kb][e], oacc[e], 0, 0, 0);
       }
     }
   };
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
-  // output: lane (col, grp) holds columns 4 grp + r of its wavefront at head_dim 8 col + e
+  // output: lane (col, grp) holds columns 4 grp + r of its wavefront at head_dim 16 e + col
   float lt = l_run;
   lt += __shfl_xor(lt, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
@@ -316,10 +322,9 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(DecodeArgs a) {
     const int h = w * 16 + 4 * grp + r;
     if ((h >> lg) < nt) {
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
-      float4* o = reinterpret_cast<float4*>(
-          out + ((size_t)(h >> lg) * a.q_heads + (h & (G - 1))) * HD + col * 8);
-      o[0] = make_float4(oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv);
-      o[1] = make_float4(oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv);
+      float* o = out + ((size_t)(h >> lg) * a.q_heads + (h & (G - 1))) * HD + col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[16 * e] = oacc[e][r] * inv;
     }
   }
 }
