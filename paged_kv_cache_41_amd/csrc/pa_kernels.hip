@@ -285,6 +285,10 @@ DecodeFn pick_generic_d(int head_dim, int group) {
 
 inline int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 
+// Tiles per wavefront at least: the start-up and the end of a range stay small next to
+// its stream (12, 16 and 30 measured no better on the batch-64 and window workloads).
+constexpr int stream_tiles_per_wave = 22;
+
 // Wavefronts of the streaming decode: one workgroup of four per compute unit of a 256-CU
 // MI355X, so the whole grid is resident at once (a second workgroup per unit measured
 // slower: more concurrent streams, each with less of its own data in flight).
@@ -475,7 +479,7 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
     const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live, run_sinks);
     // about 22 tiles per wavefront at least (so the start-up and the end of a range stay
     // small next to its stream), at most stream_waves_max
-    int64_t waves = tiles_max / 22;
+    int64_t waves = tiles_max / stream_tiles_per_wave;
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
@@ -636,7 +640,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
                              max_q, keys, nb)) {
     const int64_t tiles_max =
         stream::tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys, nb);
-    int64_t waves = tiles_max / 22;
+    int64_t waves = tiles_max / stream_tiles_per_wave;
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
