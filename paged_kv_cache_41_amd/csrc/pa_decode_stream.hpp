@@ -1,17 +1,19 @@
 // Balanced streaming decode: bf16 pools, head_dim 128, up to 16 query heads per kv head,
-// page sizes that are powers of two, up to STREAM_BMAX sequences.
+// page sizes that are powers of two, up to BMAX sequences.
 //
 // Work is the flattened list of 16-row tiles of every (sequence, kv head) segment:
-// segment (s, g) covers the tiles of rows [lo_s, L_s) aligned to 16-row boundaries,
-// segments are ordered by s then g.  A resident grid of W wavefronts splits that list
-// into W contiguous ranges of equal length, so every wavefront streams the same number
-// of tiles with no per-item start-up, no empty work items and no ragged tail.  A range
-// can cross segment boundaries; the pipeline crosses them too.
+// segment (s, g) covers the tiles of its attended rows aligned to 16-row boundaries (with
+// attention sinks, the sink rows' tiles and then the window's), segments ordered by s then
+// g.  A resident grid of W wavefronts splits that list into W contiguous ranges of equal
+// length, so every wavefront streams the same number of tiles with no per-item start-up,
+// no empty work items and no ragged tail.  A range can cross segment boundaries; the
+// pipeline crosses them too.
 //
 // Every workgroup first turns the context lengths into per-sequence tile counts and an
-// exclusive prefix sum in LDS.  Each wavefront then runs a three-stage software pipeline over its tiles: the block-table
-// entry of tile i+3 (one per lane, for token t0 + lane % 16), the K and V rows of tile
-// i+2, and the compute of tile i.  All loads are unconditional: a row outside the
+// exclusive prefix sum in LDS.  Each wavefront then runs a three-stage software pipeline
+// over its tiles: the block-table entry of tile i+3 (one per tile, read through the scalar
+// unit, for pages of at least 16 rows; one per lane for smaller pages), the K and V rows
+// of tile i+2, and the compute of tile i.  All loads are unconditional: a row outside the
 // attended range or behind an unmapped entry is read from a clamped address inside the
 // pool and masked out of the softmax and P.V; past the end of the range the last tile
 // is re-read (a cache hit).
@@ -36,11 +38,11 @@
 // wavefront; the wavefront that finishes a cut segment's last piece combines its pieces in
 // a fixed order.
 //
-// Several query tokens per sequence (MULTI): the 16 score columns are 16 / G consecutive
-// query tokens times the G heads of the group, so a segment is (block of query tokens,
-// kv head) and covers the rows the block's first query may attend up to its last query's
-// own row; each column is masked to its own query's rows (causal, window counted from
-// that query).
+// Several query tokens per sequence (MULTI, NB > 0): the score columns are NB blocks of
+// 16 / G consecutive query tokens times the G heads of the group, so a segment is (group
+// of query tokens, kv head) and covers the rows the group's first query may attend up to
+// its last query's own row; each column is masked to its own query's rows (causal, window
+// counted from that query), and the NB blocks share every K/V tile and V operand gather.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,8 +80,9 @@ constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
 struct Tile {
   uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
   uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
-  uint4 q[4];        // query head lane % 16, bytes [64 (lane / 16), +64): loaded with the
-                     // tile that opens a segment piece only
+  uint4 q[4];        // query column lane % 16, bytes [64 (lane / 16), +64): loaded with the
+                     // tile that opens a segment piece only (groups of more than one block
+                     // read their queries at the segment start instead)
   uint64_t valid;    // bit t (t < 16): token t0 + t is attended and mapped
 };
 
