@@ -19,10 +19,11 @@
 // is re-read (a cache hit).
 //
 // Compute per tile runs on the matrix cores twice.  Scores: four
-// v_mfma_f32_16x16x32_bf16 with the K tile as the A operand (row = token, lane l holds
-// 64 contiguous bytes of token l % 16; the sum over head_dim is order-free, so lane
-// group l / 16 takes head_dim slice [32 (l / 16), +32)) and the group's queries as the
-// B operand (column = query head), leaving lane l with the scores of query head l % 16
+// v_mfma_f32_16x16x32_bf16 with the K tile as the A operand (row = token; the sum over
+// head_dim is order-free, so in product j lane l takes the 8 elements at 32 j + 8 (l / 16)
+// of token l % 16, and each load reads 64 contiguous bytes of every token) and the
+// group's queries, in the same order, as the B operand (column = query head), leaving
+// lane l with the scores of query head l % 16
 // for tokens 4 (l / 16) .. +3.  Softmax in base 2 with a lazily raised reference max
 // then gives each lane the probabilities of exactly those four tokens for its head,
 // which is the A-operand layout of v_mfma_f32_16x16x16_bf16 (row = head, k = token).
@@ -78,9 +79,10 @@ constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
 #endif
 
 struct Tile {
-  uint4 k[4];        // K: token (lane % 16), bytes [64 (lane / 16), +64) of its head row
+  uint4 k[4];        // K: token (lane % 16), bytes [64 j + 16 (lane / 16), +16) of its
+                     // head row in k[j]
   uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
-  uint4 q[4];        // query column lane % 16, bytes [64 (lane / 16), +64): loaded with the
+  uint4 q[4];        // query column lane % 16, the same bytes as k: loaded with the
                      // tile that opens a segment piece only (groups of more than one block
                      // read their queries at the segment start instead)
   uint64_t valid;    // bit t (t < 16): token t0 + t is attended and mapped
@@ -459,10 +461,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
                                           ((uint32_t)(t & (P - 1)) * row_bytes + lane_off));
   };
 
-  // K rows of token t0 + col (64 B at slice grp), V rows of tokens t0 + 4 grp + j (16 B
-  // at column block col).  When a tile lies inside one page (page size >= 16: tiles start
+  // K rows of token t0 + col (16 B at byte 64 j + 16 grp for product j: the four lanes of
+  // a token read 64 contiguous bytes per load), V rows of tokens t0 + 4 grp + j (16 B at
+  // column block col).  When a tile lies inside one page (page size >= 16: tiles start
   // at multiples of 16) the per-lane byte offsets are the same for every tile.
-  const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 64;
+  const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 16;
   const uint32_t v_lane_off = (uint32_t)(4 * grp) * row_bytes + col * 16;
 
   auto load_tile = [&](const Desc& d, int e, Tile& Tl) {
@@ -479,9 +482,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         qr = (size_t)d.s * a.q_heads + (size_t)d.g * G + (col < G ? col : 0);
       }
       const uint4* qrow = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(a.q) + qr * HD + grp * 32);
+          reinterpret_cast<const uint16_t*>(a.q) + qr * HD + grp * 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Tl.q[j] = qrow[j];
+      for (int j = 0; j < 4; ++j) Tl.q[j] = qrow[4 * j];
     }
     if constexpr (PAGE_TILES) {
       // one page for the whole tile: a uniform base address plus constant lane offsets
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
                             (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)d.g * HD * 2;
       const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
+      for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
       const char* vb = vbase + base + v_lane_off;
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
@@ -506,9 +509,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
                0xffffull;
     const uint32_t hoff = (uint32_t)d.g * HD * 2;
     const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
-    const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 64);
+    const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Tl.k[j] = kp[j];
+    for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ev = __shfl(e, 4 * grp + j, 64);
@@ -570,9 +573,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
           const uint4* qrow = reinterpret_cast<const uint4*>(
               reinterpret_cast<const uint16_t*>(a.q) +
               ((size_t)(q0 + (cval[i] ? tq : 0)) * a.q_heads + (size_t)d.g * G +
-               (col & (G - 1))) * HD + grp * 32);
+               (col & (G - 1))) * HD + grp * 8);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) qb[i][j] = as_bf16x8(cval[i] ? qrow[j] : zero);
+          for (int j = 0; j < 4; ++j) qb[i][j] = as_bf16x8(cval[i] ? qrow[4 * j] : zero);
         }
       }
     }

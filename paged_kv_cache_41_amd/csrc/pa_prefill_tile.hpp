@@ -12,7 +12,7 @@
 // leave registers and LDS for three workgroups per compute unit.  Each wavefront reads the keys and
 // values from LDS in matrix-core operand layouts: scores with v_mfma_f32_16x16x32_bf16
 // (A = 16 keys x 32 of head_dim, B = the 16 columns' queries), base-2 online softmax with
-// a lazily raised reference max, P.V with v_mfma_f32_16x16x16_bf16 (P as bf16 high part
+// a lazily raised reference max, P.V with v_mfma_f32_16x16x32_bf16 (P as bf16 high part
 // plus bf16 remainder; the V operand read with transposing LDS reads, ds_read_b64_tr_b16,
 // which hand each lane one head_dim column of four key rows).  Each column is masked to its own query's rows (causal, the window counted
 // from its row); a block that every column attends skips the masks.  A workgroup
@@ -44,6 +44,7 @@ constexpr int HD = 128;
 #endif
 constexpr int KT = PTILE_KT;      // key rows per block
 constexpr int NKB = KT / 16;      // blocks of 16 rows in a matrix-core product
+static_assert(NKB % 2 == 0, "P.V takes the key blocks in pairs");
 constexpr int TPR = 256 / KT;     // lanes loading one key row
 constexpr int UPT = KT / 16;      // 16-byte pieces of K (and of V) each lane loads
 #ifndef PTILE_WG_PER_CU
@@ -271,23 +272,36 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
       }
     }
     const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+    // P.V over 32 keys per product (v_mfma_f32_16x16x32_bf16): the A operand of lane
+    // (col, grp) holds column col's probabilities of keys 4 grp + r of two 16-row blocks,
+    // and the B operand the same keys' values (the two transposing reads of those blocks),
+    // so both sides take the keys in the same order
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float p[4];
+    for (int kp = 0; kp < NKB / 2; ++kp) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = cval ? __builtin_amdgcn_exp2f(sv[kb][r] - ms) : 0.f;
-        l_run += p[r];
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * kp + h;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = cval ? __builtin_amdgcn_exp2f(sv[kb][r] - ms) : 0.f;
+          l_run += p[r];
+        }
+        hw[2 * h] = pack_bf16(p[0], p[1]);
+        hw[2 * h + 1] = pack_bf16(p[2], p[3]);
+        lw[2 * h] = pack_bf16(p[0] - bf16_lo(hw[2 * h]), p[1] - bf16_hi(hw[2 * h]));
+        lw[2 * h + 1] = pack_bf16(p[2] - bf16_lo(hw[2 * h + 1]), p[3] - bf16_hi(hw[2 * h + 1]));
       }
-      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
-      const uint32_t l01 = pack_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-      const uint32_t l23 = pack_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-      const bf16x4 phi = __builtin_bit_cast(bf16x4, make_uint2(h01, h23));
-      const bf16x4 plo_ = __builtin_bit_cast(bf16x4, make_uint2(l01, l23));
+      const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 plo_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb[kb][e], oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo_, vb[kb][e], oacc[e], 0, 0, 0);
+        const uint2 v0 = __builtin_bit_cast(uint2, vb[2 * kp][e]);
+        const uint2 v1 = __builtin_bit_cast(uint2, vb[2 * kp + 1][e]);
+        const bf16x8 bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo_, bv, oacc[e], 0, 0, 0);
       }
     }
   };
