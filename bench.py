@@ -332,7 +332,8 @@ def main():
     if multi:
         need = ops.prefill_workspace_bytes(sc.q, sc.q_start, kv_view[0], kv_view[1],
                                            sc.block_tables, sc.context_lens, max_q_len=max_q,
-                                           window=s.window, max_context_len=sc.max_context_len)
+                                           window=s.window, scale=sc.scale,
+                                           max_context_len=sc.max_context_len)
     else:
         need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
                                           sc.context_lens, window=s.window, sinks=s.sinks,
@@ -471,10 +472,11 @@ def main():
     kernel = (f"{call} call: decode_stream_kernel (one launch)" if streaming else
               f"{call} call: per-row kernels and merge")
     if multi:
-        tiles = s.num_seqs * s.kv_heads * -(-max_q // (64 // G)) if (G & (G - 1)) == 0 else 0
+        # the tile kernel: 128 score columns per workgroup, two workgroups per compute unit
+        tiles = s.num_seqs * s.kv_heads * -(-max_q // (128 // G)) if (G & (G - 1)) == 0 else 0
         if (s.dtype == "bf16" and s.head_dim == 128 and G <= 16 and (G & (G - 1)) == 0 and
                 (sc.table_page_size & (sc.table_page_size - 1)) == 0 and max_q * G >= 128 and
-                tiles >= 1024):
+                tiles >= 512):
             kernel = "pa_prefill call: prefill_tile_kernel (one launch)"
     # the bound: matrix cores when the call does more flops per byte than the ridge point
     if flops / nb["total"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):

@@ -173,6 +173,8 @@ int pa_decode_sinks(float* out, const void* q, const void* k_pool, const void* v
  *   queries than rows) gets a zero row.  n = 1 everywhere is pa_decode.
  *   max_q_len     host upper bound on the query tokens of one sequence (sizes
  *                 the grid and the workspace); rows beyond it are not written.
+ *   The workspace size depends on the shape, max_q_len and the sign of scale:
+ *   query it with the arguments of the call.
  *   Every other argument, the workspace rules (zeros before the first use,
  *   left ready by every call; no overlapping calls on one workspace) and the
  *   supported shapes are those of pa_decode; there are no sink rows here.

@@ -613,8 +613,8 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   a.qscale = scale * 1.4426950408889634f;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  // long chunks: a workgroup per tile of 64 query columns, K/V shared through LDS
-  if (ptile::eligible(dtype, head_dim, group, page_size, num_seqs, kv_heads, max_q)) {
+  // long chunks: a workgroup per tile of 128 query columns, K/V shared through LDS
+  if (ptile::eligible(dtype, head_dim, group, page_size, num_seqs, kv_heads, max_q, scale)) {
     if (!workspace) {
       *workspace_bytes = 0;
       return PA_OK;

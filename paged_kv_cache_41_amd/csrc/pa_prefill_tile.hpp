@@ -25,6 +25,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa.h"
 #include "pa_common.hpp"
 #include "pa_decode_mfma.hpp"
@@ -47,19 +49,42 @@ constexpr int NKB = KT / 16;      // blocks of 16 rows in a matrix-core product
 static_assert(NKB % 2 == 0, "P.V takes the key blocks in pairs");
 constexpr int TPR = 256 / KT;     // lanes loading one key row
 constexpr int UPT = KT / 16;      // 16-byte pieces of K (and of V) each lane loads
-#ifndef PTILE_WG_PER_CU
-#define PTILE_WG_PER_CU 3
+#ifndef PTILE_CB
+#define PTILE_CB 2
 #endif
-constexpr int COLS = 64;          // score columns per workgroup
-#ifndef PTILE_ROWB
-#define PTILE_ROWB (256 + 32)
+constexpr int CB = PTILE_CB;      // blocks of 16 score columns per wavefront
+constexpr int COLS = 64 * CB;     // score columns per workgroup
+#ifndef PTILE_WG_PER_CU
+#define PTILE_WG_PER_CU (CB == 1 ? 3 : 2)
 #endif
 #ifndef PTILE_DIE_MAJOR
 #define PTILE_DIE_MAJOR 1
 #endif
+#ifndef PTILE_SWZ
+#define PTILE_SWZ 1
+#endif
+#if PTILE_SWZ
+// LDS holds a key row in 256 bytes, its 16-byte chunks permuted within the row: chunk ch
+// of row r sits at chunk ch ^ swz(r).  The LDS has 64 banks of 4 bytes and serves 256
+// bytes per cycle: sixteen lanes of a 16-byte access, thirty-two of an 8-byte one.  swz
+// takes all sixteen values on rows 16k .. 16k + 15 (a K read: one chunk of sixteen rows)
+// and, on rows 8k .. 8k + 7, values whose bits 1-3 differ (a transposing V read: chunks
+// 2e and 2e + 1 of eight rows), so neither touches a bank twice; the staging writes
+// (sixteen lanes: half a row each of two rows, the halves crossed between even and odd
+// rows) land on sixteen different chunks too.
+constexpr int ROWB = 256;
+__device__ __forceinline__ int swz(int row) { return ((row << 1) & 15) | ((row >> 3) & 1); }
+#else
+#ifndef PTILE_ROWB
+#define PTILE_ROWB (256 + 32)
+#endif
 constexpr int ROWB = PTILE_ROWB;  // LDS bytes per key row (one kv head's 256 bytes, padded)
+__device__ __forceinline__ int swz(int) { return 0; }
+#endif
 // byte offset of 16-byte chunk `ch` (0..15) of key row `row` in an LDS buffer
-__device__ __forceinline__ int lds_off(int row, int ch) { return row * ROWB + (ch << 4); }
+__device__ __forceinline__ int lds_off(int row, int ch) {
+  return row * ROWB + ((ch ^ swz(row)) << 4);
+}
 constexpr float RESCALE_T = 8.f;
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -121,25 +146,32 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
     return;
   }
 
-  // this lane's column: head (c & (G - 1)) of query token c >> lg of the tile
-  const int c = w * 16 + col;
-  const int tq = c >> lg;
-  const bool cval = tq < nt;
-  const int pc = p0 + tq;
-  const int pc_lo = a.window > 0 ? pc - a.window : (-0x7fffffff - 1);
+  // this lane's column of block cb: head (c & (G - 1)) of query token c >> lg of the tile,
+  // c = 16 (CB w + cb) + col
+  bool cval[CB];
+  int pc[CB], pc_lo[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int tq = (16 * (CB * w + cb) + col) >> lg;
+    cval[cb] = tq < nt;
+    pc[cb] = p0 + tq;
+    pc_lo[cb] = a.window > 0 ? pc[cb] - a.window : (-0x7fffffff - 1);
+  }
   // a block of rows [k0, k0 + KT) with k0 + KT - 1 <= pmin and k0 > plo is attended by all
   const int pmin = p0;
   const int plo = a.window > 0 ? p0 + nt - 1 - a.window : (-0x7fffffff - 1);
 
-  bf16x8 qb[4];
-  {
+  bf16x8 qb[CB][4];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
+    const int c = 16 * (CB * w + cb) + col;
+    const int tq = cval[cb] ? c >> lg : 0;
     const uint4* qrow = reinterpret_cast<const uint4*>(
         reinterpret_cast<const uint16_t*>(a.q) +
-        ((size_t)(q0 + tk0 + (cval ? tq : 0)) * a.q_heads + (size_t)g * G + (c & (G - 1))) * HD +
-        grp * 32);
+        ((size_t)(q0 + tk0 + tq) * a.q_heads + (size_t)g * G + (c & (G - 1))) * HD + grp * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(cval ? qrow[j] : zero);
+    for (int j = 0; j < 4; ++j) qb[cb][j] = as_bf16x8(cval[cb] ? qrow[j] : zero);
   }
 
   const int P = a.page_size;
@@ -152,8 +184,8 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   const int last_page = a.num_pages - 1;
 
   // loading: lane tid takes key row kk = tid / TPR of the block, 16-byte pieces
-  // UPT part .. UPT part + UPT - 1 of it
-  const int kk = tid / TPR, part = tid % TPR;
+  // part + TPR (i ^ (kk & 1)) of it, i < UPT
+  const int kk = tid / TPR, part = tid % TPR, hx = kk & 1;
   const int kt0 = lo & ~(KT - 1);
   const int nblk = (kend - 1 - kt0) / KT + 1;
   // (the key of block b is written out in each lambda: a lambda that calls another one
@@ -166,62 +198,72 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
     const int key = min(max(kt0 + b * KT + kk, lo), kend - 1);
     const int pg = min(max(e, 0), last_page);
     const size_t off = (size_t)(uint32_t)pg * page_bytes + (size_t)(key & (P - 1)) * row_bytes +
-                       part * UPT * 16;
+                       part * 16;
     const uint4* kp = reinterpret_cast<const uint4*>(kbase + off);
     const uint4* vp = reinterpret_cast<const uint4*>(vbase + off);
-    rk0 = kp[0];
-    rk1 = kp[1];
-    rv0 = vp[0];
-    rv1 = vp[1];
+    rk0 = kp[TPR * (0 ^ hx)];
+    rk1 = kp[TPR * (1 ^ hx)];
+    rv0 = vp[TPR * (0 ^ hx)];
+    rv1 = vp[TPR * (1 ^ hx)];
     if constexpr (UPT > 2) {
-      rk2 = kp[2];
-      rk3 = kp[3];
-      rv2 = vp[2];
-      rv3 = vp[3];
+      rk2 = kp[TPR * (2 ^ hx)];
+      rk3 = kp[TPR * (3 ^ hx)];
+      rv2 = vp[TPR * (2 ^ hx)];
+      rv3 = vp[TPR * (3 ^ hx)];
     }
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
     char* kd = lds_k[buf];
     char* vd = lds_v[buf];
-    const int c0 = part * UPT;
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 0)) = rk0;
-    *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 1)) = rk1;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 0)) = rv0;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 1)) = rv1;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (0 ^ hx))) = rk0;
+    *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (1 ^ hx))) = rk1;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (0 ^ hx))) = rv0;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (1 ^ hx))) = rv1;
     if constexpr (UPT > 2) {
-      *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 2)) = rk2;
-      *reinterpret_cast<uint4*>(kd + lds_off(kk, c0 + 3)) = rk3;
-      *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 2)) = rv2;
-      *reinterpret_cast<uint4*>(vd + lds_off(kk, c0 + 3)) = rv3;
+      *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (2 ^ hx))) = rk2;
+      *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (3 ^ hx))) = rk3;
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (2 ^ hx))) = rv2;
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (3 ^ hx))) = rv3;
     }
   };
 
-  float m_ref = -INFINITY, l_run = 0.f;
-  f32x4 oacc[8];
+  float m_ref[CB], l_run[CB];
+  f32x4 oacc[CB][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb) {
+    m_ref[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[cb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  auto compute = [&](int b, int buf) __attribute__((always_inline)) {
+  // compute block b from LDS buffer buf (a constant at every call, so the buffer's offset
+  // folds into the LDS instructions); MASKED: some column does not attend every row
+  auto compute = [&](auto masked, int b, int buf) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int k0 = kt0 + b * KT;
     const char* Ks = lds_k[buf];
     const char* Vs = lds_v[buf];
-    // scores of the block's rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col.
-    // All K fragments of the block are read first, so their LDS latency overlaps.
+    // scores of the block's rows: lane (col, grp) gets rows 16 kb + 4 grp + r of column col
+    // of each column block.  All K fragments of the block are read first, so their LDS
+    // latency overlaps, and serve every column block.
     uint4 kf[NKB][4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         kf[kb][j] = *reinterpret_cast<const uint4*>(Ks + lds_off(kb * 16 + col, 4 * grp + j));
-    f32x4 sc[NKB];
+    f32x4 sc[CB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][j]), qb[j], sc[kb], 0,
-                                                         0, 0);
-    }
+      for (int kb = 0; kb < NKB; ++kb) {
+        sc[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][j]), qb[cb][j],
+                                                               sc[cb][kb], 0, 0, 0);
+      }
     // The P.V operand of head_dim 16 e .. 16 e + 15, read now (in flight during the
     // softmax) with transposing LDS reads: in each group of 16 lanes, lane L reads 4
     // consecutive values of key row 4 grp + L / 4 at head_dim 16 e + 4 (L % 4), and the read
@@ -232,76 +274,76 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vb[kb][e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) bf16x4*)(Vs + (kb * 16 + 4 * grp + (col >> 2)) * ROWB +
-                                                        32 * e + 8 * (col & 3)));
-    float sv[NKB][4];
-    float mt = -INFINITY;
-    // a block every column attends takes no masks (a uniform branch); in the others each
-    // score is kept or set to -inf with a select, not a branch
-    if (k0 + KT - 1 <= pmin && k0 > plo) {
+            (__attribute__((address_space(3))) bf16x4*)(
+                Vs + lds_off(kb * 16 + 4 * grp + (col >> 2), 2 * e + ((col >> 1) & 1)) +
+                8 * (col & 1)));
+    // Scores stay unscaled: the scale (times log2 e, positive on this path) multiplies the
+    // block max once and enters each exponent through one fused multiply-add.  Masked
+    // blocks set the scores of rows a column does not attend to -inf with selects.
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float sv[NKB][4];
+      float mr = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sv[kb][r] = sc[kb][r] * a.qscale;
-          mt = fmaxf(mt, sv[kb][r]);
+          if constexpr (MASKED) {
+            const int t = k0 + kb * 16 + 4 * grp + r;
+            const bool ok = (t <= pc[cb]) & (t > pc_lo[cb]);
+            sv[kb][r] = ok ? sc[cb][kb][r] : -INFINITY;
+          } else {
+            sv[kb][r] = sc[cb][kb][r];
+          }
+          mr = fmaxf(mr, sv[kb][r]);
         }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      float mt = mr * a.qscale;
+      if (__ballot(cval[cb] && mt > m_ref[cb] + RESCALE_T) != 0) {
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m_ref[cb], mt);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[cb] - mn);
+        l_run[cb] *= alpha;
+        m_ref[cb] = mn;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = k0 + kb * 16 + 4 * grp + r;
-          const bool ok = (t <= pc) & (t > pc_lo);
-          sv[kb][r] = ok ? sc[kb][r] * a.qscale : -INFINITY;
-          mt = fmaxf(mt, sv[kb][r]);
+          const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oacc[cb][e][r] *= ar;
         }
-    }
-    if (__ballot(cval && mt > m_ref + RESCALE_T) != 0) {
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m_ref, mt);
-      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
-      l_run *= alpha;
-      m_ref = mn;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * grp + r, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[e][r] *= ar;
       }
-    }
-    const float ms = m_ref == -INFINITY ? 0.f : m_ref;
-    // P.V over 32 keys per product (v_mfma_f32_16x16x32_bf16): the A operand of lane
-    // (col, grp) holds column col's probabilities of keys 4 grp + r of two 16-row blocks,
-    // and the B operand the same keys' values (the two transposing reads of those blocks),
-    // so both sides take the keys in the same order
+      const float ms = m_ref[cb] == -INFINITY ? 0.f : m_ref[cb];
+      // P.V over 32 keys per product (v_mfma_f32_16x16x32_bf16): the A operand of lane
+      // (col, grp) holds column col's probabilities of keys 4 grp + r of two 16-row blocks,
+      // and the B operand the same keys' values (the two transposing reads of those
+      // blocks), so both sides take the keys in the same order
 #pragma unroll
-    for (int kp = 0; kp < NKB / 2; ++kp) {
-      uint32_t hw[4], lw[4];
+      for (int kp = 0; kp < NKB / 2; ++kp) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kb = 2 * kp + h;
-        float p[4];
+        for (int h = 0; h < 2; ++h) {
+          const int kb = 2 * kp + h;
+          float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = cval ? __builtin_amdgcn_exp2f(sv[kb][r] - ms) : 0.f;
-          l_run += p[r];
+          for (int r = 0; r < 4; ++r) {
+            p[r] = cval[cb] ? __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms)) : 0.f;
+            l_run[cb] += p[r];
+          }
+          hw[2 * h] = pack_bf16(p[0], p[1]);
+          hw[2 * h + 1] = pack_bf16(p[2], p[3]);
+          lw[2 * h] = pack_bf16(p[0] - bf16_lo(hw[2 * h]), p[1] - bf16_hi(hw[2 * h]));
+          lw[2 * h + 1] = pack_bf16(p[2] - bf16_lo(hw[2 * h + 1]), p[3] - bf16_hi(hw[2 * h + 1]));
         }
-        hw[2 * h] = pack_bf16(p[0], p[1]);
-        hw[2 * h + 1] = pack_bf16(p[2], p[3]);
-        lw[2 * h] = pack_bf16(p[0] - bf16_lo(hw[2 * h]), p[1] - bf16_hi(hw[2 * h]));
-        lw[2 * h + 1] = pack_bf16(p[2] - bf16_lo(hw[2 * h + 1]), p[3] - bf16_hi(hw[2 * h + 1]));
-      }
-      const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8 plo_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8 plo_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint2 v0 = __builtin_bit_cast(uint2, vb[2 * kp][e]);
-        const uint2 v1 = __builtin_bit_cast(uint2, vb[2 * kp + 1][e]);
-        const bf16x8 bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo_, bv, oacc[e], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const uint2 v0 = __builtin_bit_cast(uint2, vb[2 * kp][e]);
+          const uint2 v1 = __builtin_bit_cast(uint2, vb[2 * kp + 1][e]);
+          const bf16x8 bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+          oacc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, oacc[cb][e], 0, 0, 0);
+          oacc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo_, bv, oacc[cb][e], 0, 0, 0);
+        }
       }
     }
   };
@@ -316,8 +358,32 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   load(min(1, bl), e1);
   int e2 = entry(min(2, bl));
   __syncthreads();
-  for (int b = 0; b < nblk; ++b) {
-    compute(b, b & 1);
+  // Blocks [pb1, pb2) are attended by every column (past the window start of the last
+  // query, up to the first query's row) and take no masks; the blocks before and after
+  // them do.  Three loops, so that each holds one copy of the block's code.
+  const int pb1 = min(plo < kt0 ? 0 : (plo - kt0) / KT + 1, nblk);
+  const int pb2 = min(max(max(pmin - kt0 + 1, 0) / KT, pb1), nblk);
+  int b = 0;
+  for (; b < pb1; ++b) {
+    compute(std::true_type{}, b, b & 1);
+    if (b + 1 < nblk) {
+      stage((b + 1) & 1);
+      load(min(b + 2, bl), e2);
+      e2 = entry(min(b + 3, bl));
+    }
+    __syncthreads();
+  }
+  for (; b < pb2; ++b) {
+    compute(std::false_type{}, b, b & 1);
+    if (b + 1 < nblk) {
+      stage((b + 1) & 1);
+      load(min(b + 2, bl), e2);
+      e2 = entry(min(b + 3, bl));
+    }
+    __syncthreads();
+  }
+  for (; b < nblk; ++b) {
+    compute(std::true_type{}, b, b & 1);
     if (b + 1 < nblk) {
       stage((b + 1) & 1);
       load(min(b + 2, bl), e2);
@@ -326,35 +392,40 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
     __syncthreads();
   }
 
-  // output: lane (col, grp) holds columns 4 grp + r of its wavefront at head_dim 16 e + col
-  float lt = l_run;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  // output: lane (col, grp) holds columns 4 grp + r of each column block at head_dim
+  // 16 e + col
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float lr = __shfl(lt, 4 * grp + r, 64);
-    const int h = w * 16 + 4 * grp + r;
-    if ((h >> lg) < nt) {
-      const float inv = lr > 0.f ? 1.f / lr : 0.f;
-      float* o = out + ((size_t)(h >> lg) * a.q_heads + (h & (G - 1))) * HD + col;
+  for (int cb = 0; cb < CB; ++cb) {
+    float lt = l_run[cb];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[16 * e] = oacc[e][r] * inv;
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(lt, 4 * grp + r, 64);
+      const int h = 16 * (CB * w + cb) + 4 * grp + r;
+      if ((h >> lg) < nt) {
+        const float inv = lr > 0.f ? 1.f / lr : 0.f;
+        float* o = out + ((size_t)(h >> lg) * a.q_heads + (h & (G - 1))) * HD + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[16 * e] = oacc[cb][e][r] * inv;
+      }
     }
   }
 }
 
-// Tiles per sequence at most and the grid; the path serves chunks of at least two tiles'
-// worth of query columns with enough workgroups to cover the chip.
+// Tiles per sequence at most and the grid; the path serves chunks of at least 128 query
+// columns with a workgroup for every slot of the chip at least.
+constexpr int MIN_GRID = 256 * PTILE_WG_PER_CU;
 inline int64_t grid_size(int num_seqs, int kv_heads, int group, int max_q) {
   const int tpt = COLS / group;
   return (int64_t)num_seqs * kv_heads * ((max_q + tpt - 1) / tpt);
 }
 inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_seqs,
-                     int kv_heads, int max_q) {
-  return dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
+                     int kv_heads, int max_q, float scale) {
+  return scale > 0.f && dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
          (group & (group - 1)) == 0 && page_size > 0 && (page_size & (page_size - 1)) == 0 &&
-         num_seqs >= 1 && (int64_t)max_q * group >= 2 * COLS &&
-         grid_size(num_seqs, kv_heads, group, max_q) >= 1024 &&
+         num_seqs >= 1 && (int64_t)max_q * group >= 128 &&
+         grid_size(num_seqs, kv_heads, group, max_q) >= MIN_GRID &&
          grid_size(num_seqs, kv_heads, group, max_q) < ((int64_t)1 << 31);
 }
 

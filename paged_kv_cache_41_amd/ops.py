@@ -162,10 +162,14 @@ def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, m
 
 
 def prefill_workspace_bytes(q, q_start, k_pool, v_pool, block_tables, context_lens, *,
-                            max_q_len: int, window: int = 0, max_context_len: int = 0) -> int:
-    """Bytes of device workspace ``prefill`` needs for these operands."""
+                            max_q_len: int, window: int = 0, scale: Optional[float] = None,
+                            max_context_len: int = 0) -> int:
+    """Bytes of device workspace ``prefill`` needs for these operands (and scale: the
+    kernel that serves long chunks needs none, and takes positive scales only)."""
+    if scale is None:
+        scale = int(q.shape[-1]) ** -0.5
     return _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens,
-                         max_q_len, window, 1.0, max_context_len, None, 0, None)
+                         max_q_len, window, scale, max_context_len, None, 0, None)
 
 
 def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len: int,

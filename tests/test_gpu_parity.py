@@ -210,7 +210,7 @@ MULTI = {
 }
 
 
-# Long chunks over enough (sequence, kv head, 64-column) tiles: the tile kernel with K/V
+# Long chunks over enough (sequence, kv head, 128-column) tiles: the tile kernel with K/V
 # staged through LDS.
 MULTI_TILE = {
     "tile_g4_p16": dict(_GQA, num_seqs=16, page_size=16, len_lo=130, len_hi=700, q_lo=60,
@@ -235,8 +235,8 @@ def test_prefill_tile(name):
                                         **MULTI_TILE[name]), 47, device="cuda")
     s = sc.spec
     G = s.q_heads // s.kv_heads
-    tiles = s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (64 // G))
-    assert tiles >= 1024 and int(sc.nq.max()) * G >= 128    # the tile path's conditions
+    tiles = s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (128 // G))
+    assert tiles >= 512 and int(sc.nq.max()) * G >= 128    # the tile path's conditions
     check_step(sc)
 
 
@@ -271,7 +271,7 @@ def test_prefill_more_queries_than_rows():
     assert int(sc.nq.max()) * 4 < 128 and len(sc.q) >= 170
     for path in ("stream", "tile"):
         # the bound on query tokens picks the path: the shape's own bound (under 32 tokens)
-        # streams; 170 makes 24 x 8 x 11 tiles of 16 tokens, enough for the tile kernel
+        # streams; 170 makes 24 x 8 x 6 tiles of 32 tokens, enough for the tile kernel
         mq = {"stream": max(int(sc.nq.max()), 1), "tile": 170}[path]
         out = o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, ctx,
                         max_q_len=mq, scale=sc.scale).cpu().double().numpy()
