@@ -94,9 +94,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+#ifndef PTILE_LPT
+#define PTILE_LPT 1
+#endif
+constexpr int LPT_MAX = 128;    // sequences ordered longest first (more: in index order)
+
 __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
   __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
+#if PTILE_LPT
+  __shared__ int lpt_key[LPT_MAX];
+  __shared__ int lpt_seq[LPT_MAX];
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,7 +128,48 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   }
 #endif
   const int qt = wid % QT;
-  const int sg = wid / QT;
+  int sg = wid / QT;
+#if PTILE_LPT
+  if (a.num_seqs <= LPT_MAX) {
+    // Longest first: workgroups start in number order within a die, and the work per
+    // (sequence, kv head) unit follows its attended rows, which vary widely; starting the
+    // longest units first keeps a long one from running alone at the end.  Units are taken
+    // in order of their sequence's attended rows (ties by index) and dealt round-robin over
+    // the dies' runs of work: run x holds units x, x + 8, x + 16, ... of that order.
+    const int B = a.num_seqs;
+    for (int t = tid; t < B; t += 256) {
+      const int q0t = a.q_start[t];
+      int nq = a.q_start[t + 1] - q0t;
+      if (q0t < 0 || q0t > a.num_q) nq = 0;
+      nq = max(0, min(min(nq, a.num_q - q0t), a.max_q));
+      const int ct = a.ctx[t];
+      const int Lt = ct > 0 ? (ct < a.max_ctx ? ct : a.max_ctx) : 0;
+      lpt_key[t] = nq > 0 ? (a.window > 0 ? min(Lt, a.window + nq) : Lt) : -1;
+    }
+    __syncthreads();
+    for (int t = tid; t < B; t += 256) {
+      const int kt = lpt_key[t];
+      int r = 0;
+      for (int u = 0; u < B; ++u) {
+        const int ku = lpt_key[u];
+        r += (ku > kt) | ((ku == kt) & (u < t));
+      }
+      lpt_seq[r] = t;
+    }
+    __syncthreads();
+    const int U = B * Hkv, q8 = U >> 3, r8 = U & 7;
+    int x, i;
+    if (sg < r8 * (q8 + 1)) {
+      x = sg / (q8 + 1);
+      i = sg % (q8 + 1);
+    } else {
+      x = r8 + (sg - r8 * (q8 + 1)) / q8;
+      i = (sg - r8 * (q8 + 1)) % q8;
+    }
+    const int k = x + 8 * i;
+    sg = lpt_seq[k / Hkv] * Hkv + k % Hkv;
+  }
+#endif
   const int g = sg % Hkv;
   const int s = sg / Hkv;
 
