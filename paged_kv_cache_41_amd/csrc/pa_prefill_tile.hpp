@@ -375,8 +375,10 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
           const int kb = 2 * kp + h;
           float p[4];
 #pragma unroll
+          // (a column past the tile's queries has zero queries and finite values
+          // throughout, and its output row is never written)
           for (int r = 0; r < 4; ++r) {
-            p[r] = cval[cb] ? __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms)) : 0.f;
+            p[r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms));
             l_run[cb] += p[r];
           }
           hw[2 * h] = pack_bf16(p[0], p[1]);
