@@ -240,6 +240,45 @@ def test_prefill_tile(name):
     check_step(sc)
 
 
+def _tile_shape(sc):
+    s = sc.spec
+    G = s.q_heads // s.kv_heads
+    return (s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (128 // G)) >= 512 and
+            int(sc.nq.max()) * G >= 128)
+
+
+def _prefill_ws(sc, scale):
+    return ops().prefill_workspace_bytes(sc.q, sc.q_start, sc.k_pool, sc.v_pool,
+                                         sc.block_tables, sc.context_lens,
+                                         max_q_len=max(int(sc.nq.max()), 1),
+                                         window=sc.spec.window, scale=scale,
+                                         max_context_len=sc.max_context_len)
+
+
+def test_prefill_tile_shape_negative_scale():
+    # The tile kernel takes the block max of unscaled scores, so it serves positive
+    # scales only; a negative one on the same long chunks goes to the streaming kernel
+    # (which needs a workspace, the tile kernel none).
+    kw = dict(MULTI_TILE["tile_g4_p16_w100"])
+    sc = workloads.build(workloads.Spec(name="prefill_tile_negscale", pool_factor=1.25,
+                                        scale=-0.0625, **kw), 53, device="cuda")
+    assert _tile_shape(sc) and sc.scale < 0
+    assert _prefill_ws(sc, 0.0625) == 0 and _prefill_ws(sc, sc.scale) > 0
+    check_step(sc)
+
+
+def test_prefill_tile_many_sequences():
+    # more sequences than the tile kernel ranks (128): its work stays in index order
+    spec = workloads.Spec(name="prefill_tile_b160", **_GQA, num_seqs=160, page_size=16,
+                          len_lo=40, len_hi=300, q_lo=33, q_hi=40, pool_factor=1.25)
+    sc = workloads.build(spec, 59, device="cuda")
+    assert _tile_shape(sc) and sc.spec.num_seqs > 128
+    assert _prefill_ws(sc, sc.scale) == 0
+    rng = np.random.default_rng(5)
+    rows = sorted(set(rng.choice(len(sc.q), 240, replace=False).tolist()) | {0, len(sc.q) - 1})
+    check_step(sc, seqs=rows)
+
+
 @pytest.mark.parametrize("name", sorted(MULTI))
 def test_prefill(name):
     sc = workloads.build(workloads.Spec(name=f"prefill_{name}", pool_factor=1.25,
