@@ -1,24 +1,27 @@
 // Prefill chunks: several query tokens per sequence, many of them (bf16 pools, head_dim
-// 128, G = q_heads / kv_heads a power of two up to 16, page sizes that are powers of two).
+// 128, G = q_heads / kv_heads a power of two up to 16, page sizes that are powers of two,
+// a positive scale).
 //
-// One workgroup of four wavefronts per (sequence, kv head, tile of 64 score columns); a
+// One workgroup of four wavefronts per (sequence, kv head, tile of 128 score columns); a
 // column is one query head of one query token (column c: head c % G of token c / G of the
-// tile), so a tile holds 64 / G query tokens.  Wavefront w takes columns 16 w .. 16 w + 15.
+// tile), so a tile holds 128 / G query tokens.  Wavefront w takes two blocks of 16
+// columns, 32 w .. 32 w + 31, so every K and V fragment it reads from LDS feeds both.
 // The workgroup walks the key rows its tile's queries attend, from the window start of
 // its first query to its last query's own row, 32 rows at a time: the K and V rows of the
 // next 32 are loaded by all 256 lanes (each lane 32 bytes of K and of V) while the current
 // ones are computed, and written to one of two LDS buffers, so every K/V byte is read from
-// memory once per tile and shared by its 64 columns.  Blocks of 32 rows (rather than 64)
-// leave registers and LDS for three workgroups per compute unit.  Each wavefront reads the keys and
-// values from LDS in matrix-core operand layouts: scores with v_mfma_f32_16x16x32_bf16
-// (A = 16 keys x 32 of head_dim, B = the 16 columns' queries), base-2 online softmax with
-// a lazily raised reference max, P.V with v_mfma_f32_16x16x32_bf16 (P as bf16 high part
-// plus bf16 remainder; the V operand read with transposing LDS reads, ds_read_b64_tr_b16,
-// which hand each lane one head_dim column of four key rows).  Each column is masked to its own query's rows (causal, the window counted
-// from its row); a block that every column attends skips the masks.  A workgroup
-// covers its tile's whole key range, so there is no split and nothing to merge; every key
-// row loaded lies in [window start of the first query, last query's row], which are rows
-// some query attends, so every table entry read is a mapped page.
+// memory once per tile and shared by its 128 columns.  Two workgroups share a compute
+// unit.  Each wavefront reads the keys and values from LDS in matrix-core operand
+// layouts: scores with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 of head_dim, B = 16
+// columns' queries), base-2 online softmax with a lazily raised reference max, P.V with
+// v_mfma_f32_16x16x32_bf16 over 32 keys (P as bf16 high part plus bf16 remainder; the V
+// operand read with transposing LDS reads, ds_read_b64_tr_b16, which hand each lane one
+// head_dim column of four key rows).  Each column is masked to its own query's rows
+// (causal, the window counted from its row); the blocks every column attends run in a
+// loop of their own without masks.  A workgroup covers its tile's whole key range, so
+// there is no split and nothing to merge; every key row loaded lies in [window start of
+// the first query, last query's row], which are rows some query attends, so every table
+// entry read is a mapped page.  Units of work start longest first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,10 +63,6 @@ constexpr int COLS = 64 * CB;     // score columns per workgroup
 #ifndef PTILE_DIE_MAJOR
 #define PTILE_DIE_MAJOR 1
 #endif
-#ifndef PTILE_SWZ
-#define PTILE_SWZ 1
-#endif
-#if PTILE_SWZ
 // LDS holds a key row in 256 bytes, its 16-byte chunks permuted within the row: chunk ch
 // of row r sits at chunk ch ^ swz(r).  The LDS has 64 banks of 4 bytes and serves 256
 // bytes per cycle: sixteen lanes of a 16-byte access, thirty-two of an 8-byte one.  swz
@@ -74,13 +73,6 @@ constexpr int COLS = 64 * CB;     // score columns per workgroup
 // rows) land on sixteen different chunks too.
 constexpr int ROWB = 256;
 __device__ __forceinline__ int swz(int row) { return ((row << 1) & 15) | ((row >> 3) & 1); }
-#else
-#ifndef PTILE_ROWB
-#define PTILE_ROWB (256 + 32)
-#endif
-constexpr int ROWB = PTILE_ROWB;  // LDS bytes per key row (one kv head's 256 bytes, padded)
-__device__ __forceinline__ int swz(int) { return 0; }
-#endif
 // byte offset of 16-byte chunk `ch` (0..15) of key row `row` in an LDS buffer
 __device__ __forceinline__ int lds_off(int row, int ch) {
   return row * ROWB + ((ch ^ swz(row)) << 4);
