@@ -85,7 +85,7 @@ struct Tile {
   uint4 q[4];        // query column lane % 16, the same bytes as k: loaded with the
                      // tile that opens a segment piece only (groups of more than one block
                      // read their queries at the segment start instead)
-  uint64_t valid;    // bit t (t < 16): token t0 + t is attended and mapped
+  uint32_t valid;    // bit t (t < 16): token t0 + t is attended and mapped (uniform)
 };
 
 // Two floats rounded to bf16 (nearest even) and packed, low element first.
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 
   auto load_tile = [&](const Desc& d, int e, Tile& Tl) {
     const int t0 = d.t0;
-    if (NB <= 1 && (d.flags & (RANGE_FIRST | SEG_FIRST))) {
+    if (NB <= 1 && (uni(d.flags) & (RANGE_FIRST | SEG_FIRST))) {
       // the query rows of the group, fetched with the tile so that waiting for them is
       // waiting for this tile; lanes past the group read head 0 and are zeroed later
       size_t qr;
@@ -488,14 +488,17 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     }
     if constexpr (PAGE_TILES) {
       // one page for the whole tile: a uniform base address plus constant lane offsets
+      // (the descriptor's fields are the same in every lane: read as such, the mask and
+      // the base address are scalar work)
       const int pg = uni(e);
+      const int ut0 = uni(t0), ulo = uni(d.lo), uL = uni(d.L), usl = uni(d.sl), ug = uni(d.g);
       const bool mapped = pg >= 0 && pg <= last_page;
-      const int lo_off = min(max(d.lo - t0, 0), TILE), hi_off = min(d.L - t0, TILE);
-      const int sl_off = min(max(d.sl - t0, 0), TILE);
+      const int lo_off = min(max(ulo - ut0, 0), TILE), hi_off = min(uL - ut0, TILE);
+      const int sl_off = min(max(usl - ut0, 0), TILE);
       const uint32_t bits = ((1u << hi_off) - 1u) & (~((1u << lo_off) - 1u) | ((1u << sl_off) - 1u));
-      Tl.valid = mapped ? (uint64_t)bits : 0ull;
+      Tl.valid = mapped ? bits : 0u;
       const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
-                            (uint32_t)(t0 & (P - 1)) * row_bytes + (uint32_t)d.g * HD * 2;
+                            (uint32_t)(ut0 & (P - 1)) * row_bytes + (uint32_t)ug * HD * 2;
       const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
@@ -505,8 +508,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       return;
     }
     const int tk = t0 + col;
-    Tl.valid = __ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e >= 0 && e <= last_page) &
-               0xffffull;
+    Tl.valid = (uint32_t)(__ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e >= 0 &&
+                                   e <= last_page) & 0xffffull);
     const uint32_t hoff = (uint32_t)d.g * HD * 2;
     const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
     const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 16);
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) oacc[i][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    started_here = (d.flags & SEG_FIRST) != 0;
+    started_here = (uni(d.flags) & SEG_FIRST) != 0;
   };
 
   auto end_segment = [&](const Desc& d, bool complete) {
@@ -662,7 +665,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   };
 
   auto compute = [&](const Tile& Tl, const Desc& d) {
-    if (d.flags & (RANGE_FIRST | SEG_FIRST)) begin_segment(d, Tl);
+    // the tile's flags and row mask are the same in every lane: read them as such, so
+    // the branches on them are scalar
+    const int flags = uni(d.flags);
+    const uint32_t valid = (uint32_t)uni((int)Tl.valid);
+    if (flags & (RANGE_FIRST | SEG_FIRST)) begin_segment(d, Tl);
     // scores S[token][column] = K . q, one product per block of 16 columns
     f32x4 sc[NBX];
 #pragma unroll
@@ -674,7 +681,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
                                                         0);
     }
     // a tile whose rows every column attends needs no masks (most tiles of long contexts)
-    bool plain = Tl.valid == 0xffffull;
+    bool plain = valid == 0xffffu;
     if constexpr (MULTI) plain = plain && d.t0 + 15 <= seg_pmin && d.t0 > seg_plo;
     bf16x4 phi[NBX], plo[NBX];
 #pragma unroll
@@ -690,7 +697,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          bool ok = (Tl.valid >> (4 * grp + r)) & 1;
+          bool ok = (valid >> (4 * grp + r)) & 1;
           if constexpr (MULTI) {
             const int t = d.t0 + 4 * grp + r;
             ok = ok && t <= pc[i] && t > pc_lo[i];
@@ -735,10 +742,10 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     // (rows of the last page past the sequence end are never written): replace them by
     // zeros, since 0 * NaN would poison the product.
     uint4 vt[4] = {Tl.v[0], Tl.v[1], Tl.v[2], Tl.v[3]};
-    if (Tl.valid != 0xffffull) {
+    if (valid != 0xffffu) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!((Tl.valid >> (4 * grp + j)) & 1)) vt[j] = make_uint4(0, 0, 0, 0);
+        if (!((valid >> (4 * grp + j)) & 1)) vt[j] = make_uint4(0, 0, 0, 0);
     }
     const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
     const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
@@ -758,8 +765,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[i], bv, oacc[i][e], 0, 0, 0);
       }
     }
-    if (d.flags & (SEG_LAST | RANGE_LAST))
-      end_segment(d, (d.flags & SEG_LAST) && started_here);
+    if (flags & (SEG_LAST | RANGE_LAST))
+      end_segment(d, (flags & SEG_LAST) && started_here);
   };
 
   // ---- pipeline: table entry DEPTH+1 tiles ahead, K/V DEPTH tiles ahead, compute ------
@@ -792,9 +799,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       fr.next();
       load_tile(d_use, e_use, buf[(u + DEPTH) % (DEPTH + 1)]);
       dsc[(u + DEPTH) % (DEPTH + 1)] = d_use;
-      if (!(dsc[u].flags & IDLE)) compute(buf[u], dsc[u]);
+      if (!(uni(dsc[u].flags) & IDLE)) compute(buf[u], dsc[u]);
     }
-    if (dsc[DEPTH].flags & IDLE) break;
+    if (uni(dsc[DEPTH].flags) & IDLE) break;
   }
 
   // ---- cut segments: the piece that arrives last combines them ---------------------------
