@@ -77,6 +77,27 @@ def test_config_full(index):
     check_step(sc)
 
 
+@pytest.mark.parametrize("q_len", [4, 128, 512])
+def test_config_prefill_chunks_sampled(q_len):
+    # the workloads `bench.py --q-len N` times, at full size, in the same launch: the
+    # 4-token verify streams, the 128- and 512-token chunks take the tile kernel with its
+    # longest-first order; sampled query rows, the first and last of the call included
+    base = workloads.config_spec(2)
+    sc = workloads.make_config(2, device="cuda", q_lo=q_len, q_hi=q_len,
+                               name=f"{base.name}_q{q_len}")
+    assert int(sc.nq.max()) == q_len
+    rng = np.random.default_rng(q_len)
+    rows = sorted(set(rng.choice(len(sc.q), 64, replace=False).tolist()) | {0, len(sc.q) - 1})
+    check_step(sc, seqs=rows)
+
+
+def test_config_window_sinks_full():
+    # `bench.py --config 3 --sinks 4`: every sequence, every row
+    base = workloads.config_spec(3)
+    sc = workloads.make_config(3, device="cuda", sinks=4, name=f"{base.name}_sinks4")
+    check_step(sc)
+
+
 def test_config_prefix_sampled():
     sc = workloads.make_config(4, device="cuda")
     assert len(sc.copy_src) > 200
