@@ -481,7 +481,7 @@ def test_table_updates_prefill_with_pages():
 @pytest.mark.parametrize("seed", range(4))
 def test_table_updates_keep_device_tables_in_step(seed):
     """Random lifecycles (sinks, forks, copy-on-write, trims, rewinds, releases,
-    rolled-back steps): tables kept only by scattering each round's updates equal
+    rolled-back steps): tables kept only by scattering each step's updates equal
     the tables rebuilt from the allocator, on every readable row."""
     R = random.Random(200 + seed)
     P, NP, ROWS, STRIDE = 4, 48, 6, 40
