@@ -355,7 +355,7 @@ def test_prefill_single_token_equals_decode():
     assert float((a - b).abs().max()) <= 1e-5
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(60))
 def test_random_small(seed):
     sc = workloads.build(workloads.random_spec(seed), seed, device="cuda")
     check_step(sc)
@@ -384,7 +384,7 @@ def _random_multi_spec(seed):
                           pool_factor=1.5)
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(36))
 def test_random_prefill(seed):
     spec = _random_multi_spec(seed)
     sc = workloads.build(spec, 2000 + seed, device="cuda")
