@@ -475,7 +475,7 @@ def main():
         # the tile kernel: 128 score columns per workgroup, two workgroups per compute unit
         tiles = s.num_seqs * s.kv_heads * -(-max_q // (128 // G)) if (G & (G - 1)) == 0 else 0
         if (s.dtype == "bf16" and s.head_dim == 128 and G <= 16 and (G & (G - 1)) == 0 and
-                (sc.table_page_size & (sc.table_page_size - 1)) == 0 and max_q * G >= 128 and
+                (sc.table_page_size & (sc.table_page_size - 1)) == 0 and max_q * G >= 48 and
                 tiles >= 512):
             kernel = "pa_prefill call: prefill_tile_kernel (one launch)"
     # the bound: matrix cores when the call does more flops per byte than the ridge point

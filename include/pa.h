@@ -117,7 +117,9 @@ int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_pages,
  *   attended rows, with fp32 accumulation.
  *   workspace     device scratch of *workspace_bytes bytes.  With workspace ==
  *                 NULL the call only stores the required size in
- *                 *workspace_bytes and returns PA_OK.  It must hold zeros
+ *                 *workspace_bytes and returns PA_OK, also when that size is
+ *                 0: a call that needs no workspace still takes a non-NULL
+ *                 pointer to run.  It must hold zeros
  *                 before its first use (it carries counters that the kernel
  *                 counts up and puts back to zero); every completed call
  *                 leaves it ready for the next one, whatever the shapes.

@@ -89,7 +89,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 #ifndef PTILE_LPT
 #define PTILE_LPT 1
 #endif
-constexpr int LPT_MAX = 128;    // sequences ordered longest first (more: in index order)
+constexpr int LPT_MAX = 256;    // sequences ordered longest first (more: in index order)
 
 __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
@@ -457,8 +457,10 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   }
 }
 
-// Tiles per sequence at most and the grid; the path serves chunks of at least 128 query
-// columns with a workgroup for every slot of the chip at least.
+// Tiles per sequence at most and the grid; the path serves chunks of at least 48 query
+// columns (12 tokens at G = 4: below that the streaming kernel, which does not pad the
+// columns to a 128-column tile, is faster) with a workgroup for every slot of the chip.
+constexpr int MIN_COLS = 48;
 constexpr int MIN_GRID = 256 * PTILE_WG_PER_CU;
 inline int64_t grid_size(int num_seqs, int kv_heads, int group, int max_q) {
   const int tpt = COLS / group;
@@ -468,7 +470,7 @@ inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_
                      int kv_heads, int max_q, float scale) {
   return scale > 0.f && dtype == PA_BF16 && head_dim == HD && group >= 1 && group <= 16 &&
          (group & (group - 1)) == 0 && page_size > 0 && (page_size & (page_size - 1)) == 0 &&
-         num_seqs >= 1 && (int64_t)max_q * group >= 128 &&
+         num_seqs >= 1 && (int64_t)max_q * group >= MIN_COLS &&
          grid_size(num_seqs, kv_heads, group, max_q) >= MIN_GRID &&
          grid_size(num_seqs, kv_heads, group, max_q) < ((int64_t)1 << 31);
 }

@@ -137,7 +137,10 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
         raise ValueError("out must be a contiguous fp32 [num_seqs, q_heads, head_dim]")
     need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, sinks,
                         scale, max_context_len, None, 0, None)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    # (an empty tensor's pointer is NULL, which the library reads as a size query: even
+    # when the call needs no workspace it gets a byte of its own)
+    if workspace is None or workspace.numel() == 0 or \
+            workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, workspace.data_ptr(),
@@ -204,7 +207,10 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
         raise ValueError("out must be a contiguous fp32 [num_q, q_heads, head_dim]")
     need = _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
                          window, scale, max_context_len, None, 0, None)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    # (an empty tensor's pointer is NULL, which the library reads as a size query: even
+    # when the call needs no workspace it gets a byte of its own)
+    if workspace is None or workspace.numel() == 0 or \
+            workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, window,
                   scale, max_context_len, workspace.data_ptr(),

@@ -257,7 +257,7 @@ def test_prefill_tile(name):
     s = sc.spec
     G = s.q_heads // s.kv_heads
     tiles = s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (128 // G))
-    assert tiles >= 512 and int(sc.nq.max()) * G >= 128    # the tile path's conditions
+    assert tiles >= 512 and int(sc.nq.max()) * G >= 48    # the tile path's conditions
     check_step(sc)
 
 
@@ -265,7 +265,7 @@ def _tile_shape(sc):
     s = sc.spec
     G = s.q_heads // s.kv_heads
     return (s.num_seqs * s.kv_heads * -(-int(sc.nq.max()) // (128 // G)) >= 512 and
-            int(sc.nq.max()) * G >= 128)
+            int(sc.nq.max()) * G >= 48)
 
 
 def _prefill_ws(sc, scale):
@@ -288,12 +288,32 @@ def test_prefill_tile_shape_negative_scale():
     check_step(sc)
 
 
+def test_empty_workspace_tensor_still_computes():
+    # the tile kernel needs no workspace; an empty tensor (NULL pointer) must not turn
+    # the call into a size query that leaves the output unwritten
+    sc = workloads.build(workloads.Spec(name="prefill_tile_emptyws", pool_factor=1.25,
+                                        **MULTI_TILE["tile_g4_p16"]), 61, device="cuda")
+    assert _tile_shape(sc) and _prefill_ws(sc, sc.scale) == 0
+    o = ops()
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    mq = int(sc.nq.max())
+    kw = dict(max_q_len=mq, window=sc.spec.window, scale=sc.scale,
+              max_context_len=sc.max_context_len)
+    ref = o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+                    **kw)
+    out = torch.full_like(ref, float("nan"))
+    empty = torch.zeros(0, dtype=torch.uint8, device="cuda")
+    o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+              out=out, workspace=empty, **kw)
+    assert torch.equal(out, ref)
+
+
 def test_prefill_tile_many_sequences():
-    # more sequences than the tile kernel ranks (128): its work stays in index order
-    spec = workloads.Spec(name="prefill_tile_b160", **_GQA, num_seqs=160, page_size=16,
+    # more sequences than the tile kernel ranks (256): its work stays in index order
+    spec = workloads.Spec(name="prefill_tile_b300", **_GQA, num_seqs=300, page_size=16,
                           len_lo=40, len_hi=300, q_lo=33, q_hi=40, pool_factor=1.25)
     sc = workloads.build(spec, 59, device="cuda")
-    assert _tile_shape(sc) and sc.spec.num_seqs > 128
+    assert _tile_shape(sc) and sc.spec.num_seqs > 256
     assert _prefill_ws(sc, sc.scale) == 0
     rng = np.random.default_rng(5)
     rows = sorted(set(rng.choice(len(sc.q), 240, replace=False).tolist()) | {0, len(sc.q) - 1})
@@ -328,10 +348,11 @@ def test_prefill_more_queries_than_rows():
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
     ctx = sc.context_lens.clone()
     ctx[::2] = torch.as_tensor(sc.nq[::2] // 2, device="cuda", dtype=torch.int32)
-    assert int(sc.nq.max()) * 4 < 128 and len(sc.q) >= 170
+    assert int(sc.nq.max()) <= 32 and len(sc.q) >= 170
     for path in ("stream", "tile"):
-        # the bound on query tokens picks the path: the shape's own bound (under 32 tokens)
-        # streams; 170 makes 24 x 8 x 6 tiles of 32 tokens, enough for the tile kernel
+        # the bound on query tokens picks the path: the shape's own bound (at most 32
+        # tokens: 24 x 8 tiles, fewer than the tile kernel takes) streams; 170 makes
+        # 24 x 8 x 6 tiles of 32 tokens, enough for the tile kernel
         mq = {"stream": max(int(sc.nq.max()), 1), "tile": 170}[path]
         out = o.prefill(sc.q, sc.q_start, sc.k_pool, sc.v_pool, sc.block_tables, ctx,
                         max_q_len=mq, scale=sc.scale).cpu().double().numpy()
