@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "pa.h"
 #include "pa_common.hpp"
@@ -831,15 +832,17 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
   const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
   if (!last0 && !last1) return;
-  // One wavefront combines a segment, CPP columns per pass: lane l takes head_dim
-  // (128 / CPP) ... of column l / (64 / CPP) (+ CPP per pass); the partials of
-  // COMBINE_BATCH pieces are loaded together.  Decode (at most 16 columns, usually a few)
-  // takes 4 columns per pass, several query tokens (16 or 32 columns) 8, which needs more
-  // registers.
+  // One wavefront combines a segment, CPP columns per pass: lane l of the NL lanes doing
+  // it takes head_dim QPL floats of column l / LPC (+ CPP per pass), LPC = NL / CPP; the
+  // partials of COMBINE_BATCH pieces are loaded together.  Decode (at most 16 columns,
+  // usually a few) takes 4 columns per pass, several query tokens (16 or 32 columns) 8.
+  // A decode wavefront that combines both of its segments gives each one half of its
+  // lanes, so that the loads of the two combines are in flight together.
   constexpr int CPP = MULTI ? 8 : 4;
-  constexpr int LPC = 64 / CPP;             // lanes per column
-  constexpr int QPL = HD / LPC / 4;         // float4 per lane
-  auto combine = [&](int seg, int k1, int k2) {
+  auto combine = [&](auto nl_c, int sl, int seg, int k1, int k2) {
+    constexpr int NL = decltype(nl_c)::value;
+    constexpr int LPC = NL / CPP;             // lanes per column
+    constexpr int QPL = HD / LPC / 4;         // float4 per lane
     const int s = seg / Hkv, g = seg % Hkv;
     const int tiles = st_cum[s + 1] - st_cum[s];
     const int seg_start = Hkv * st_cum[s] + g * tiles;
@@ -851,8 +854,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       out = a.out + ((size_t)st_q0[s] * a.q_heads + (size_t)g * G) * HD;
       ncols = st_nt[s] << lg;
     }
-    const int cd = (lane % LPC) * (QPL * 4);
-    for (int h = lane / LPC; h < ncols; h += CPP) {
+    const int cd = (sl % LPC) * (QPL * 4);
+    for (int h = sl / LPC; h < ncols; h += CPP) {
       float M = -INFINITY, den = 0.f;
       float4 nm[QPL];
 #pragma unroll
@@ -893,11 +896,19 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       for (int q = 0; q < QPL; ++q)
         o[q] = make_float4(nm[q].x * inv, nm[q].y * inv, nm[q].z * inv, nm[q].w * inv);
     }
-    if (lane == 0)
+    if (sl == 0)
       __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  if (last0) combine(seg0, k1_0, k2_0);
-  if (last1) combine(seg1, k1_1, k2_1);
+  if constexpr (!MULTI) {
+    if (last0 && last1) {
+      const bool hi = lane >= 32;
+      combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0, hi ? k1_1 : k1_0,
+              hi ? k2_1 : k2_0);
+      return;
+    }
+  }
+  if (last0) combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
+  if (last1) combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
 }
 
 // Tiles of the whole list at most: max_live attended rows per sequence, of which `sinks`
