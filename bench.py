@@ -162,6 +162,30 @@ def measured_traffic(path: str, workload: str):
         return None
 
 
+def pages_unshared(sc) -> bool:
+    """True when no physical page is attended by two sequences (block tables of pages of
+    16 rows or more; a raw slot table is not checked and gets no hint)."""
+    s = sc.spec
+    if sc.table_page_size != s.page_size or s.page_size < 16:
+        return False
+    bt = sc.block_tables.cpu().numpy()
+    lens = sc.context_lens.cpu().numpy()
+    seen = set()
+    for b in range(len(lens)):
+        L = int(lens[b])
+        if L <= 0:
+            continue
+        lo = L - min(L, s.window) if s.window > 0 else 0
+        pages = set(range(lo // s.page_size, (L - 1) // s.page_size + 1))
+        if s.sinks > 0 and L > s.window:
+            pages |= set(range(0, (s.sinks - 1) // s.page_size + 1))
+        phys = {int(bt[b, j]) for j in pages}
+        if seen & phys:
+            return False
+        seen |= phys
+    return True
+
+
 def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
     """Bandwidth of a plain device-to-device copy (torch's copy kernel) of known size:
     a measured reference next to the nominal peak, and the calibration kernel for the
@@ -352,6 +376,10 @@ def main():
     nb = decode_bytes(sc)
     kv_bytes_step = nb["kv"]
 
+    # the cache hint is passed only when, checked here on the host, no physical page is
+    # attended by two sequences of the batch
+    unshared = pages_unshared(sc)
+
     def step():
         ops.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
         ops.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
@@ -364,7 +392,8 @@ def main():
         else:
             ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
                        window=s.window, sinks=s.sinks, scale=sc.scale,
-                       max_context_len=sc.max_context_len, out=out, workspace=ws)
+                       max_context_len=sc.max_context_len, out=out, workspace=ws,
+                       unshared_pages=unshared)
 
     for _ in range(args.warmup):
         step()
@@ -515,7 +544,9 @@ def main():
                             ("back-to-back steps" if args.flush == "none" else
                              "every step starts after a 1 GiB write"),
                    "launch": ("each step one HIP graph replay (copy, store, attention)"
-                              if args.graph else "kernels launched one by one")},
+                              if args.graph else "kernels launched one by one"),
+                   "cache_hint": ("unshared pages (checked on the host): V rows read with the "
+                                  "non-temporal hint" if unshared and not multi else "none")},
         "seqs_per_s": round(s.num_seqs / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * nb["kv"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "step": {"avg_us": round(float(step_ms.mean()) * 1e3, 2),

@@ -157,6 +157,27 @@ int pa_decode_sinks(float* out, const void* q, const void* k_pool, const void* v
                     int32_t dtype, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * pa_decode_hinted -- pa_decode_sinks with hints about the batch that change how
+ * the rows are read, never what is computed: the output is bit-identical to
+ * pa_decode_sinks with the same arguments.
+ *   hints         0 or PA_HINT_UNSHARED: no physical page is attended by two
+ *                 sequences of the call (no shared prefix, no fork sharing a
+ *                 page), so nothing read has a reuse worth caching; the V rows are
+ *                 then loaded with the non-temporal cache hint.  Wrong hints
+ *                 cost time, not correctness.  Used by the path for bf16 with
+ *                 head_dim 128 and page_size >= 16; ignored elsewhere.
+ *   Errors: PA_EINVAL for other hint bits; otherwise those of pa_decode_sinks.
+ */
+#define PA_HINT_UNSHARED 1
+int pa_decode_hinted(float* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t bt_stride,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                     int32_t kv_heads, int32_t head_dim, int32_t num_pages, int32_t page_size,
+                     int32_t window, int32_t sinks, int32_t hints, int32_t max_context_len,
+                     float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
+                     void* stream);
+
+/*
  * pa_prefill -- several query tokens per sequence against its cached rows: a
  * chunk of a prompt (the tiny-llm page "Paged KV Cache", section "Prefill
  * with Pages": the chunk's rows are stored into pages, here by pa_store_kv,

@@ -16,6 +16,8 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH = 0, -1, -2, -3, -4
 # every symbol include/pa.h declares, with its ctypes signature
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
+PA_HINT_UNSHARED = 1
+
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_store_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -25,6 +27,9 @@ SIGNATURES = {
     "pa_decode_sinks": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                        _I, _I, ctypes.c_float, _I, _P,
                                        ctypes.POINTER(ctypes.c_size_t), _P]),
+    "pa_decode_hinted": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                        _I, _I, _I, ctypes.c_float, _I, _P,
+                                        ctypes.POINTER(ctypes.c_size_t), _P]),
     "pa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                   _I, _I, _I, ctypes.c_float, _I, _P,
                                   ctypes.POINTER(ctypes.c_size_t), _P]),

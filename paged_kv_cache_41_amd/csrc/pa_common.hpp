@@ -30,6 +30,7 @@ struct DecodeArgs {
   // its sequence in row_seq and its context (its position + 1) in ctx.
   const int32_t* q_start;
   int num_q, max_q;
+  int hints;                   // PA_HINT_* bits of the decode call (0: none)
   const int32_t* row_seq;      // nullptr: row s reads the table row of sequence s
 };
 

@@ -297,7 +297,9 @@ struct Front {
 // NB = 0: one query token per sequence.  NB > 0 (MULTI): several query tokens per
 // sequence, taken in groups of NB blocks of 16 / G tokens; a group's NB x 16 score
 // columns share every K/V tile a wavefront loads.
-template <int DEPTH, bool PAGE_TILES, int NB>
+// VNT: the V rows are loaded with the non-temporal cache hint (pages not shared, so no
+// reuse to keep); K keeps the default policy, since its four loads per row share lines.
+template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   constexpr bool MULTI = NB > 0;
   constexpr int NBX = MULTI ? NB : 1;
@@ -504,8 +506,15 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
       const char* vb = vbase + base + v_lane_off;
+      if constexpr (VNT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
+        for (int j = 0; j < 4; ++j)
+          Tl.v[j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                                  reinterpret_cast<const i32x4*>(vb + j * row_bytes)));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
+      }
       return;
     }
     const int tk = t0 + col;
@@ -971,7 +980,9 @@ inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
 template <int NB>
 inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
   constexpr int D = NB > 0 ? STREAM_MULTI_DEPTH : STREAM_DEPTH;
-  if (a.page_size >= TILE)
+  if (a.page_size >= TILE && (a.hints & PA_HINT_UNSHARED))
+    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true>), grid, block, 0, st, a);
+  else if (a.page_size >= TILE)
     hipLaunchKernelGGL((decode_stream_kernel<D, true, NB>), grid, block, 0, st, a);
   else
     hipLaunchKernelGGL((decode_stream_kernel<D, false, NB>), grid, block, 0, st, a);

@@ -442,15 +442,15 @@ extern "C" int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_page
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
-extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
-                               const void* v_pool, const int32_t* block_tables,
-                               int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
-                               int32_t q_heads, int32_t kv_heads, int32_t head_dim,
-                               int32_t num_pages, int32_t page_size, int32_t window,
-                               int32_t sinks, int32_t max_context_len, float scale,
-                               int32_t dtype, void* workspace, size_t* workspace_bytes,
-                               void* stream) {
+static int decode_entry(float* out, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                        int32_t kv_heads, int32_t head_dim, int32_t num_pages,
+                        int32_t page_size, int32_t window, int32_t sinks, int32_t hints,
+                        int32_t max_context_len, float scale, int32_t dtype, void* workspace,
+                        size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return PA_EINVAL;
+  if (hints & ~PA_HINT_UNSHARED) return PA_EINVAL;
   if (sinks < 0 || (sinks > 0 && (window <= 0 || sinks >= window))) return PA_EINVAL;
   if (num_seqs < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || num_pages <= 0 ||
       page_size <= 0 || bt_stride <= 0)
@@ -472,6 +472,7 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
   // sink rows form a run of their own only where the window can cut a context
   const int run_sinks = window > 0 && window < max_context_len ? sinks : 0;
   DecodeArgs a{};
+  a.hints = hints;
   a.sinks = window > 0 ? sinks : 0;
   if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
                        max_live, run_sinks)) {
@@ -553,6 +554,32 @@ extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
   a.ws_acc = a.ws_ml + 2 * parts;
 
   return launch_rows(a, generic, fast, head_dim, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_decode_sinks(float* out, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t num_pages, int32_t page_size, int32_t window,
+                               int32_t sinks, int32_t max_context_len, float scale,
+                               int32_t dtype, void* workspace, size_t* workspace_bytes,
+                               void* stream) {
+  return decode_entry(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens, num_seqs,
+                      q_heads, kv_heads, head_dim, num_pages, page_size, window, sinks, 0,
+                      max_context_len, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_hinted(float* out, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_tables,
+                                int32_t bt_stride, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                int32_t head_dim, int32_t num_pages, int32_t page_size,
+                                int32_t window, int32_t sinks, int32_t hints,
+                                int32_t max_context_len, float scale, int32_t dtype,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
+  return decode_entry(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens, num_seqs,
+                      q_heads, kv_heads, head_dim, num_pages, page_size, window, sinks, hints,
+                      max_context_len, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,

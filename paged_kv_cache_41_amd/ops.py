@@ -82,7 +82,7 @@ def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
 
 
 def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
-                 max_context_len, ws_ptr, ws_size, stream_handle):
+                 max_context_len, ws_ptr, ws_size, stream_handle, hints=0):
     n, P, hkv, d = _pool_dims(k_pool, v_pool)
     B, hq, dq = (int(x) for x in q.shape)
     lib = _lib.load()
@@ -92,7 +92,10 @@ def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sin
             context_lens.data_ptr(), B, hq, hkv, d, n, P, int(window))
     tail = (int(max_context_len), float(scale), _code(q), ws_ptr, ctypes.byref(size),
             stream_handle)
-    if sinks:
+    if hints:
+        _lib.check("pa_decode_hinted",
+                   lib.pa_decode_hinted(*head, int(sinks), int(hints), *tail))
+    elif sinks:
         _lib.check("pa_decode_sinks", lib.pa_decode_sinks(*head, int(sinks), *tail))
     else:
         _lib.check("pa_decode", lib.pa_decode(*head, *tail))
@@ -109,13 +112,16 @@ def decode_workspace_bytes(q, k_pool, v_pool, block_tables, context_lens, *, win
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
            sinks: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           stream=None) -> torch.Tensor:
+           stream=None, unshared_pages: bool = False) -> torch.Tensor:
     """Single-query paged attention; returns fp32 ``[num_seqs, q_heads, head_dim]``.
 
     A raw token-slot table is passed as ``block_tables`` together with pools
     viewed in pages of one row (``pool.view(-1, 1, kv_heads, head_dim)``).
     ``sinks > 0`` (below ``window``) also attends the first ``sinks`` rows of
     every sequence, through ``pa_decode_sinks``; 0 calls ``pa_decode``.
+    ``unshared_pages=True`` promises that no physical page is attended by two
+    sequences of the batch and calls ``pa_decode_hinted``, which reads V rows with
+    the non-temporal cache hint; the result is the same bit for bit.
     A ``workspace`` passed in must be zero-filled before its first use; each call
     leaves it ready for the next.  Without one (or with one too small) a zeroed
     workspace is allocated for this call.
@@ -144,7 +150,8 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, workspace.data_ptr(),
-                 workspace.numel() * workspace.element_size(), _stream(dev, stream))
+                 workspace.numel() * workspace.element_size(), _stream(dev, stream),
+                 _lib.PA_HINT_UNSHARED if unshared_pages else 0)
     return out
 
 

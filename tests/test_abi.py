@@ -74,6 +74,12 @@ def test_argument_validation_needs_no_gpu():
     assert sink(1024, 4) == _lib.PA_OK and size.value > 0
     with_sinks = size.value
     assert sink(1024, 0) == _lib.PA_OK and size.value <= with_sinks
+    # hints: only PA_HINT_UNSHARED is defined
+    hinted = lambda hints: lib.pa_decode_hinted(
+        None, None, None, None, None, 256, None, 64, 32, 8, 128, 1000, 16, 0, 0, hints, 4096,
+        1.0, 1, None, ctypes.byref(size), None)
+    assert hinted(_lib.PA_HINT_UNSHARED) == _lib.PA_OK and size.value > 0
+    assert hinted(2) == _lib.PA_EINVAL and hinted(-1) == _lib.PA_EINVAL
     # prefill: no queries is a no-op; queries without sequences or a bound are invalid;
     # the size query works for the streaming shape and for the rows path (fp32)
     pre = lambda B, nq, mq, hq, hkv, d, dt: lib.pa_prefill(

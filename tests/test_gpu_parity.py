@@ -98,6 +98,26 @@ def test_config_window_sinks_full():
     check_step(sc)
 
 
+@pytest.mark.parametrize("cfg,sinks", [(2, 0), (3, 0), (3, 4)])
+def test_unshared_hint_is_bit_identical(cfg, sinks):
+    """pa_decode_hinted with PA_HINT_UNSHARED changes only the cache policy of the V
+    loads: its output equals the plain call's bit for bit (which the config tests pin to
+    the oracle), on the batch-64 and window workloads, with and without sinks."""
+    o = ops()
+    sc = workloads.make_config(cfg, device="cuda", sinks=sinks,
+                               name=f"{workloads.config_spec(cfg).name}_s{sinks}")
+    s = sc.spec
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    outs = []
+    for hint in (False, True, True):
+        outs.append(o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+                               window=s.window, sinks=s.sinks, scale=sc.scale,
+                               max_context_len=sc.max_context_len, unshared_pages=hint))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_config_prefix_sampled():
     sc = workloads.make_config(4, device="cuda")
     assert len(sc.copy_src) > 200
