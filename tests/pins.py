@@ -501,5 +501,50 @@ def pin_tables():
     return P
 
 
+def _held_by_hand(rows, keep_from, S, P):
+    """Pages a request keeps, counted slot by slot: a page stays while one of its P
+    slots still matters -- a sink row (below S) or a row at or after ``keep_from``,
+    a future row landing in the partly filled tail page included."""
+    slots = -(-rows // P) * P
+    return len({r // P for r in range(slots) if r < S or r >= keep_from})
+
+
+def pin_footprint():
+    """The page counts of the window rule (silicon-compiler chapter 15, sections "The
+    problem" and "Tests", check 3) and of the attention-sink variant ("Exercises",
+    exercise 3), against a slot-by-slot count on small grids: the exact counts for
+    every (rows, keep_from), and each bound equal to the most pages held at any step
+    of a long run (after the step's new row is stored, before its trim)."""
+    P_ = []
+    sh = oracle.shadow
+    for P in (1, 2, 3, 4, 5):
+        for S in range(0, 7):
+            head = -(-S // P)
+            for rows in range(0, 21):
+                for kf in range(0, rows + P + 1):
+                    want = _held_by_hand(rows, kf, S, P)
+                    got = sh.pages_exact_sinks(rows, kf, head, P)
+                    if got != want:
+                        P_.append(f"pages_exact_sinks(rows={rows}, keep_from={kf}, S={S}, "
+                                  f"P={P}) = {got}, counted {want}")
+                    if S == 0 and sh.pages_exact(rows, kf, P) != want:
+                        P_.append(f"pages_exact(rows={rows}, keep_from={kf}, P={P}) = "
+                                  f"{sh.pages_exact(rows, kf, P)}, counted {want}")
+    for P in (1, 2, 3, 4, 8):
+        for W in range(1, 17):
+            for S in range(0, W):
+                # during step L the rows from L - (W - S) on (the previous trim) and the sinks
+                peak = max(_held_by_hand(L, max(0, L - (W - S)), S, P)
+                           for L in range(1, 3 * W + 2 * P + 2))
+                if sh.sink_bound(W, S, P) != peak:
+                    P_.append(f"sink_bound(W={W}, S={S}, P={P}) = {sh.sink_bound(W, S, P)}, "
+                              f"peak counted {peak}")
+                if S == 0 and sh.window_bound(W, P) != peak:
+                    P_.append(f"window_bound(W={W}, P={P}) = {sh.window_bound(W, P)}, "
+                              f"peak counted {peak}")
+    return P_
+
+
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_window, pin_placement,
-            pin_slot_table, pin_store, pin_copy, pin_sinks, pin_prefill, pin_tables]
+            pin_slot_table, pin_store, pin_copy, pin_sinks, pin_prefill, pin_tables,
+            pin_footprint]

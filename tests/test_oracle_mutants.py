@@ -11,6 +11,7 @@ import oracle
 import pins
 from oracle import attention as A
 from oracle import kvstore as S
+from oracle import shadow as SH
 from oracle import tables as TB
 
 _live, _gather, _head, _attend = A.live_rows, A.gather, A.kv_head_of, A.attend
@@ -18,6 +19,8 @@ _rows, _gather_rows = A.attended_rows, A.gather_rows
 _qpos = A.query_position
 _upd = TB.update_tables
 _store, _copy = S.store_kv, S.copy_pages
+_exact, _exact_s = SH.pages_exact, SH.pages_exact_sinks
+_wbound, _sbound = SH.window_bound, SH.sink_bound
 
 
 def _gather_shift_page(pool, table_row, lo, hi, dtype):
@@ -119,6 +122,12 @@ MUTANTS = {
     "released cell written as page 0": (TB, "update_tables", _upd_release_as_page0),
     "slot table written with pages of one row": (TB, "update_tables", _upd_slot_page_size_one),
     "update lands one page late": (TB, "update_tables", _upd_next_page),
+    "window count rounds keep_from up": (SH, "pages_exact", lambda rows, kf, P: max(-(-rows // P) - -(-kf // P), 0) if rows > 0 else 0),
+    "sink pages trimmed with the window": (SH, "pages_exact_sinks", lambda rows, kf, head, P: _exact(rows, kf, P)),
+    "sink count releases one page more": (SH, "pages_exact_sinks", lambda rows, kf, head, P: max(_exact_s(rows, kf, head, P) - (1 if kf // P > head else 0), 0)),
+    "window bound without the partly filled page": (SH, "window_bound", lambda W, P: _wbound(W, P) - 1),
+    "sink bound without the partly filled page": (SH, "sink_bound", lambda W, S, P: _sbound(W, S, P) - 1),
+    "sink bound counts the sinks inside the window": (SH, "sink_bound", lambda W, S, P: -(-S // P) + _wbound(W, P)),
 }
 
 
