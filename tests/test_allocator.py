@@ -541,3 +541,69 @@ def test_table_updates_keep_device_tables_in_step(seed):
                 assert st[r, :L].tolist() == ref_st[i, :L].tolist(), f"seed {seed} op {step} ({op})"
         for r in free_rows:
             assert (bt[r] == -1).all() and (st[r] == DUMMY).all(), f"seed {seed} op {step}: row {r}"
+
+
+def test_unshared_flag_follows_reference_counts():
+    """The cache hint comes from the allocator: False while a fork shares a page,
+    True again once the sibling is released; plan_step reports it after its
+    copy-on-write (the private copy is unshared, a shared full page is not)."""
+    cache = PagedKVCache(32, 4)
+    cache.new("a")
+    for _ in range(6):
+        cache.append("a")
+    assert cache.unshared(["a"])
+    cache.fork("a", "b")
+    assert not cache.unshared(["a"]) and not cache.unshared(["a", "b"])
+    plan = cache.plan_step(["a"])          # row 6 lands in the shared page 1: copied
+    assert len(plan.copy_src) == 1 and not plan.unshared    # page 0 is still shared
+    cache.release("b")
+    assert cache.unshared(["a"])
+    assert cache.plan_step(["a"]).unshared
+    # once the window releases a's shared pages, neither holder shares anything
+    cache.fork("a", "c")
+    assert not cache.unshared(["c"])
+    cache.trim("a", 8)                      # a's two full pages go; c keeps them alone
+    assert cache.table("a") == [-1, -1] and cache.unshared(["a"]) and cache.unshared(["c"])
+    cache.append("a")                       # row 8 opens a fresh page
+    assert cache.unshared(["a", "c"])
+
+
+def test_adopt_registers_tables_built_elsewhere():
+    cache = PagedKVCache(16, 4, free_order=list(range(15, -1, -1)))
+    cache.adopt("x", [3, 7, 9], 10)
+    cache.adopt("y", [3, 7, 5], 9)          # shares pages 3 and 7 with x
+    assert cache.pool.ref[3] == 2 and cache.pool.ref[9] == 1 and cache.used() == 4
+    assert not cache.unshared(["x"]) and cache.unshared([]) is True
+    assert cache.translate("y", 8) == (5, 0)
+    # a windowed table: released front cells, sink page kept
+    cache.adopt("z", [1, -1, -1, 2, 4], 19, sinks=2)
+    assert cache.dropped["z"] == 2 and cache.head["z"] == 1
+    assert cache.pages["z"] == [1, 2, 4]
+    with pytest.raises(IndexError):
+        cache.translate("z", 5)
+    cache.release("x")
+    cache.release("y")
+    assert cache.unshared(["z"]) and cache.used() == 3
+    with pytest.raises(ValueError):
+        cache.adopt("bad", [0, -1, 6, -1], 14)  # two runs of released cells
+
+
+def test_plan_step_exhaustion_checked_before_any_change():
+    """A step that needs more fresh pages than are free changes nothing: neither
+    the requests that would have fitted nor the free list."""
+    cache = PagedKVCache(6, 2)
+    for r in ("a", "b"):
+        cache.new(r)
+        for _ in range(4):
+            cache.append(r)                 # 2 full pages each
+    cache.fork("a", "c")                    # c shares a's two pages
+    free = cache.pool.free
+    tables = {r: cache.table(r) for r in ("a", "b", "c")}
+    with pytest.raises(OutOfPages):
+        cache.plan_step(["a", "b", "c"])    # three fresh pages needed, two free
+    assert cache.pool.free == free and {r: cache.table(r) for r in tables} == tables
+    assert [cache.length[r] for r in ("a", "b", "c")] == [4, 4, 4]
+    with pytest.raises(ValueError):
+        cache.plan_step(["a", "a"])
+    plan = cache.plan_step(["a", "b"])
+    assert list(plan.context_lens) == [5, 5] and cache.pool.free_count() == 0
