@@ -68,6 +68,34 @@ enum pa_status {
 const char* pa_status_string(int status);
 
 /*
+ * Decode and prefill workspaces.  A call that needs a workspace (see pa_decode)
+ * takes device memory whose first PA_WORKSPACE_HEADER bytes hold arrival
+ * counters -- one per group of rows whose partial results are combined inside
+ * the launch -- and whose remaining bytes hold those partial results.  The
+ * counters must be zero when a call starts: allocate the workspace zero-filled,
+ * or call pa_reset_workspace once.  A call that runs to completion puts every
+ * counter it raised back to zero, and no path writes anything else into the
+ * header, so calls of any shape and on any path can share the workspace one
+ * after the other.  A call that does not complete (its kernel aborted, the
+ * device reset, a fault) can leave counters raised; later calls on that
+ * workspace would then return wrong results without an error, so reset the
+ * workspace before using it again.  Calls that overlap in time must not share
+ * a workspace.
+ */
+#define PA_WORKSPACE_HEADER 4096
+
+/*
+ * pa_reset_workspace -- zero the counter header of a workspace of
+ * workspace_bytes bytes (its first min(workspace_bytes, PA_WORKSPACE_HEADER)
+ * bytes), in stream order.  The partial-result area needs no clearing.
+ *   workspace     device memory, 4-byte aligned; may be NULL only with
+ *                 workspace_bytes == 0 (a no-op).
+ * Errors: PA_EINVAL for a NULL or misaligned pointer with workspace_bytes > 0,
+ * PA_ELAUNCH when the launch is rejected.
+ */
+int pa_reset_workspace(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_store_kv -- write new K/V rows into their slots.
  *   k_pool, v_pool  [num_pages, page_size, kv_heads, head_dim], written in place.
  *   k_new, v_new    [num_tokens, kv_heads, head_dim], contiguous.
@@ -119,11 +147,10 @@ int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_pages,
  *                 NULL the call only stores the required size in
  *                 *workspace_bytes and returns PA_OK, also when that size is
  *                 0: a call that needs no workspace still takes a non-NULL
- *                 pointer to run.  It must hold zeros
- *                 before its first use (it carries counters that the kernel
- *                 counts up and puts back to zero); every completed call
- *                 leaves it ready for the next one, whatever the shapes.
- *                 Calls that overlap in time must not share a workspace.
+ *                 pointer to run.  A non-zero size includes the counter
+ *                 header; the header's rules (zero before the first use,
+ *                 left zero by every completed call, reset after a call that
+ *                 did not complete) are stated above pa_reset_workspace.
  *   Supported: dtype PA_F32 or PA_BF16; head_dim 16, 32, 64, 128 or 256;
  *   q_heads / kv_heads <= 16; any page_size >= 1.
  */
@@ -198,9 +225,9 @@ int pa_decode_hinted(float* out, const void* q, const void* k_pool, const void* 
  *                 the grid and the workspace); rows beyond it are not written.
  *   The workspace size depends on the shape, max_q_len and the sign of scale:
  *   query it with the arguments of the call.
- *   Every other argument, the workspace rules (zeros before the first use,
- *   left ready by every call; no overlapping calls on one workspace) and the
- *   supported shapes are those of pa_decode; there are no sink rows here.
+ *   Every other argument, the workspace rules (the counter header described
+ *   above pa_reset_workspace) and the supported shapes are those of
+ *   pa_decode; there are no sink rows here.
  *   Errors: PA_EINVAL also for num_q > 0 with num_seqs = 0 or max_q_len <= 0.
  */
 int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_pool,

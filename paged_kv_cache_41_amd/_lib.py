@@ -17,6 +17,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH = 0, -1, -2, -3, -4
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 PA_HINT_UNSHARED = 1
+PA_WORKSPACE_HEADER = 4096
 
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -34,6 +35,7 @@ SIGNATURES = {
                                   _I, _I, _I, ctypes.c_float, _I, _P,
                                   ctypes.POINTER(ctypes.c_size_t), _P]),
     "pa_update_tables": (ctypes.c_int, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
+    "pa_reset_workspace": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
 }
 
 _lib = None

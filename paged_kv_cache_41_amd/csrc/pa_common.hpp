@@ -4,7 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Every decode and prefill workspace starts with this many bytes of arrival counters,
+// whatever path the call takes: the streaming kernel keeps one int per wavefront range
+// there (at most 1024 ranges) and every other path leaves the bytes alone, so a
+// workspace used by calls of different shapes or paths never sees partial results where
+// a later call expects counters.  Partials start right after the header.
+constexpr size_t WS_HEADER = PA_WORKSPACE_HEADER;
 
 struct DecodeArgs {
   float* out;                  // [num_seqs, q_heads, head_dim]

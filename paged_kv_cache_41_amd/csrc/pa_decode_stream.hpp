@@ -961,19 +961,18 @@ inline bool eligible_multi(int dtype, int head_dim, int group, int page_size, in
          tiles_bound_multi(num_seqs, kv_heads, group, max_q, keys, nb) < ((int64_t)1 << 30);
 }
 
-// Workspace: the arrival counters (zero between calls), then per wavefront two partial
-// slots of `cols` score columns (running max and sum, accumulator): the group's heads, or
-// 16 with several query tokens per sequence.
+// Workspace: the arrival counters in the common header (zero between calls; one per
+// range, at most WS_HEADER / 4 ranges), then per wavefront two partial slots of `cols`
+// score columns (running max and sum, accumulator): the group's heads, or 16 with
+// several query tokens per sequence.
 inline size_t workspace_bytes(int total_waves, int cols) {
   const size_t slots = (size_t)total_waves * 2 * cols;
-  const size_t counters = ((size_t)total_waves * 4 + 255) / 256 * 256;
-  return counters + slots * 2 * sizeof(float) + slots * HD * sizeof(float);
+  return WS_HEADER + slots * 2 * sizeof(float) + slots * HD * sizeof(float);
 }
 inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
   const size_t slots = (size_t)a.total_waves * 2 * cols;
-  const size_t counters = ((size_t)a.total_waves * 4 + 255) / 256 * 256;
   a.ws_arrive = reinterpret_cast<int*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counters);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + WS_HEADER);
   a.ws_acc = a.ws_ml + slots * 2;
 }
 

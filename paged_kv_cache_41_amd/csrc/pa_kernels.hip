@@ -293,6 +293,7 @@ constexpr int stream_tiles_per_wave = 22;
 // MI355X, so the whole grid is resident at once (a second workgroup per unit measured
 // slower: more concurrent streams, each with less of its own data in flight).
 constexpr int stream_waves_max = 1024;
+static_assert(stream_waves_max * sizeof(int) <= WS_HEADER, "counters must fit the header");
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -346,6 +347,15 @@ __global__ __launch_bounds__(64) void update_tables_kernel(
       }
     }
   }
+}
+
+// Zero the first n bytes of a workspace (its counter header): 4-byte stores, the odd
+// tail bytes by one thread.
+__global__ __launch_bounds__(256) void zero_header_kernel(unsigned char* p, int n) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  for (int i = threadIdx.x; i < n / 4; i += 256) w[i] = 0u;
+  if (threadIdx.x == 0)
+    for (int i = n / 4 * 4; i < n; ++i) p[i] = 0;
 }
 
 // Query row r of a prefill chunk as a row of its own: its sequence (the last s with
@@ -524,7 +534,7 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
                                 : (max_live + a.chunk - 1) / a.chunk;
   if (a.max_chunks < 1) a.max_chunks = 1;
   const size_t parts = (size_t)num_seqs * q_heads * a.max_chunks;
-  const size_t need = parts * ((size_t)head_dim + 2) * sizeof(float);
+  const size_t need = WS_HEADER + parts * ((size_t)head_dim + 2) * sizeof(float);
   if (!workspace) {
     *workspace_bytes = need;
     return PA_OK;
@@ -550,7 +560,7 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
   a.window = window > 0 ? window : 0;
   a.max_ctx = max_context_len;
   a.qscale = scale * 1.4426950408889634f;
-  a.ws_ml = reinterpret_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + WS_HEADER);
   a.ws_acc = a.ws_ml + 2 * parts;
 
   return launch_rows(a, generic, fast, head_dim, reinterpret_cast<hipStream_t>(stream));
@@ -701,7 +711,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   if (a.max_chunks < 1) a.max_chunks = 1;
   const size_t rows_bytes = ((size_t)num_q * 2 * sizeof(int32_t) + 255) / 256 * 256;
   const size_t parts = (size_t)num_q * q_heads * a.max_chunks;
-  const size_t need = rows_bytes + parts * ((size_t)head_dim + 2) * sizeof(float);
+  const size_t need = WS_HEADER + rows_bytes + parts * ((size_t)head_dim + 2) * sizeof(float);
   if (!workspace) {
     *workspace_bytes = need;
     return PA_OK;
@@ -710,7 +720,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens)
     return PA_EINVAL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_EUNSUPPORTED;
-  int32_t* row_seq = reinterpret_cast<int32_t*>(workspace);
+  int32_t* row_seq = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + WS_HEADER);
   int32_t* row_ctx = row_seq + num_q;
   hipLaunchKernelGGL(prefill_rows_kernel, dim3((unsigned)((num_q + 255) / 256)), dim3(256), 0,
                      st, q_start, context_lens, num_seqs, num_q, max_context_len, row_seq,
@@ -719,9 +729,20 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   a.ctx = row_ctx;
   a.row_seq = row_seq;
   a.num_seqs = num_q;
-  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + rows_bytes);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + WS_HEADER +
+                                     rows_bytes);
   a.ws_acc = a.ws_ml + 2 * parts;
   return launch_rows(a, generic, fast, head_dim, st);
+}
+
+extern "C" int pa_reset_workspace(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PA_EINVAL;
+  const int n = (int)(workspace_bytes < WS_HEADER ? workspace_bytes : WS_HEADER);
+  hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<unsigned char*>(workspace), n);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
 extern "C" int pa_update_tables(int32_t* block_tables, int32_t bt_stride, int32_t bt_rows,

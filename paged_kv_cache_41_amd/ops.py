@@ -81,6 +81,17 @@ def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
         int(src_pages.numel()), n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
 
 
+def reset_workspace(workspace: torch.Tensor, stream=None) -> None:
+    """Zero the counter header of a decode/prefill workspace (``pa_reset_workspace``),
+    in stream order: needed before reusing a workspace whose last call did not complete
+    (a freshly zero-filled workspace needs nothing)."""
+    dev = _dev(workspace)
+    lib = _lib.load()
+    _lib.check("pa_reset_workspace", lib.pa_reset_workspace(
+        workspace.data_ptr() if workspace.numel() else None,
+        workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+
+
 def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, ws_ptr, ws_size, stream_handle, hints=0):
     n, P, hkv, d = _pool_dims(k_pool, v_pool)
@@ -122,9 +133,10 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     ``unshared_pages=True`` promises that no physical page is attended by two
     sequences of the batch and calls ``pa_decode_hinted``, which reads V rows with
     the non-temporal cache hint; the result is the same bit for bit.
-    A ``workspace`` passed in must be zero-filled before its first use; each call
-    leaves it ready for the next.  Without one (or with one too small) a zeroed
-    workspace is allocated for this call.
+    A ``workspace`` passed in must be zero-filled before its first use (or reset
+    with ``reset_workspace``); each completed call leaves it ready for the next,
+    whatever its shape.  Without one (or with one too small) a zeroed workspace is
+    allocated for this call.
     """
     dev = _dev(q, k_pool, v_pool, block_tables, context_lens)
     n, P, hkv, d = _pool_dims(k_pool, v_pool)

@@ -108,3 +108,21 @@ def test_argument_validation_needs_no_gpu():
 def test_package_imports_without_a_gpu():
     import paged_kv_cache_41_amd as pkg
     assert callable(pkg.ops.decode) and callable(pkg.ops.store_kv) and callable(pkg.ops.copy_pages)
+
+
+def test_reset_workspace_validation_needs_no_gpu():
+    lib = _lib.load()
+    assert lib.pa_reset_workspace(None, 0, None) == _lib.PA_OK
+    assert lib.pa_reset_workspace(None, 4096, None) == _lib.PA_EINVAL
+    assert lib.pa_reset_workspace(ctypes.c_void_p(2), 4096, None) == _lib.PA_EINVAL
+
+
+def test_every_workspace_size_includes_the_counter_header():
+    lib = _lib.load()
+    size = ctypes.c_size_t(0)
+    # streaming path (bf16, head_dim 128), per-row matrix-core path (bf16, head_dim 64),
+    # VALU path (fp32)
+    for dtype, d in ((1, 128), (1, 64), (0, 128)):
+        assert lib.pa_decode(None, None, None, None, None, 256, None, 3, 8, 2, d, 100, 16, 0,
+                             64, 1.0, dtype, None, ctypes.byref(size), None) == _lib.PA_OK
+        assert size.value > _lib.PA_WORKSPACE_HEADER, (dtype, d)

@@ -118,21 +118,19 @@ def test_unshared_hint_is_bit_identical(cfg, sinks):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-def test_config_prefix_sampled():
+def test_config_prefix_full():
+    # every sequence of the prefix-shared workload: 243 copy-on-write copies, the store,
+    # then decode over the 128 shared prefix pages and each private suffix
     sc = workloads.make_config(4, device="cuda")
     assert len(sc.copy_src) > 200
-    rng = np.random.default_rng(0)
-    seqs = sorted(set(rng.choice(256, 48, replace=False).tolist()) |
-                  {int(np.argmax(sc.lens)), int(np.argmin(sc.lens))})
-    check_step(sc, seqs=seqs)
+    check_step(sc)
 
 
-def test_config_slot_table_sampled():
+def test_config_slot_table_full():
+    # every sequence of the raw slot-table workload (page-size-1 addressing, lognormal
+    # lengths up to 32768)
     sc = workloads.make_config(5, device="cuda")
-    rng = np.random.default_rng(1)
-    seqs = sorted(set(rng.choice(256, 10, replace=False).tolist()) |
-                  {int(np.argmax(sc.lens)), int(np.argmin(sc.lens))})
-    check_step(sc, seqs=seqs)
+    check_step(sc)
 
 
 @pytest.mark.parametrize("window", [0, 40])
@@ -518,32 +516,92 @@ def test_short_contexts_under_large_bound():
     assert float(np.max(np.abs(got - ref))) <= TOL["bf16"]
 
 
-def test_workspace_reused_across_calls():
-    # the chunk ticket counter lives in the workspace: it must start over on every call
-    sc = workloads.make_config(2, device="cuda")
+def _run_on_workspace(sc, ws, max_context_len=None):
+    """copy -> store -> attention of ``sc`` with the caller's workspace and an output
+    filled with NaN first (a row the call fails to write shows), checked against the
+    oracle; then the workspace's counter header must read zero again."""
     o = ops()
+    print(f"case {sc.spec.name} seed {sc.seed} max_context_len {max_context_len}", flush=True)
+    kp0, vp0 = bits(sc.k_pool), bits(sc.v_pool)
+    o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
-    need = o.decode_workspace_bytes(sc.q, sc.k_pool, sc.v_pool, sc.block_tables,
-                                    sc.context_lens, max_context_len=sc.max_context_len)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    run = lambda: o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
-                           scale=sc.scale, max_context_len=sc.max_context_len,
-                           workspace=ws).clone()
-    first = run()
-    for _ in range(3):
-        assert torch.equal(run(), first), "a call with a reused workspace differs"
-    small = workloads.make_config(2, device="cuda", num_seqs=5)
-    assert o.decode_workspace_bytes(small.q, small.k_pool, small.v_pool, small.block_tables,
-                                    small.context_lens,
-                                    max_context_len=small.max_context_len) <= need
-    o.store_kv(small.k_pool, small.v_pool, small.k_new, small.v_new, small.slot_mapping)
-    got = o.decode(small.q, small.k_pool, small.v_pool, small.block_tables, small.context_lens,
-                   scale=small.scale, max_context_len=small.max_context_len, workspace=ws)
+    kv, vv = decode_views(sc)
+    s = sc.spec
+    out = torch.full((len(sc.q), s.q_heads, s.head_dim), float("nan"), device="cuda")
+    bound = max_context_len or sc.max_context_len
+    if sc.q_start is not None:
+        o.prefill(sc.q, sc.q_start, kv, vv, sc.block_tables, sc.context_lens,
+                  max_q_len=max(int(sc.nq.max()), 1), window=s.window, scale=sc.scale,
+                  max_context_len=bound, out=out, workspace=ws)
+    else:
+        o.decode(sc.q, kv, vv, sc.block_tables, sc.context_lens, window=s.window,
+                 sinks=s.sinks, scale=sc.scale, max_context_len=bound, out=out, workspace=ws)
     torch.cuda.synchronize()
-    _, _, ref = expected_step(small)
-    # expected_step replays copy and store on the already stored pools: identical rows
-    assert float(np.max(np.abs(got.cpu().double().numpy() - ref))) <= TOL["bf16"]
-    assert torch.equal(run(), first)
+    _, _, ref = expected_step(sc, k_pool_bits=kp0, v_pool_bits=vp0)
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all(), f"{s.name}: a row was not written"
+    assert float(np.max(np.abs(got - ref))) <= TOL[s.dtype], s.name
+    header = ws[:4096].cpu()
+    assert int(header.count_nonzero()) == 0, f"{s.name}: counters left raised"
+    return out
+
+
+def _need(sc, max_context_len=None):
+    o = ops()
+    kv, vv = decode_views(sc)
+    s = sc.spec
+    bound = max_context_len or sc.max_context_len
+    if sc.q_start is not None:
+        return o.prefill_workspace_bytes(sc.q, sc.q_start, kv, vv, sc.block_tables,
+                                         sc.context_lens, max_q_len=max(int(sc.nq.max()), 1),
+                                         window=s.window, scale=sc.scale, max_context_len=bound)
+    return o.decode_workspace_bytes(sc.q, kv, vv, sc.block_tables, sc.context_lens,
+                                    window=s.window, sinks=s.sinks, max_context_len=bound)
+
+
+def test_workspace_shared_by_every_path():
+    """One workspace, zero-filled once, serves calls of every path and shape in turn:
+    the per-row fp32 decode and prefill paths (partials right after the counter
+    header), streaming decode with few wavefronts then many (small batch, then the
+    batch-64 workload with a growing max_context_len), and streaming verify steps.
+    Every call is checked against the oracle with a NaN-filled output, and leaves the
+    counter header at zero."""
+    tiny = workloads.make_config(1, device="cuda")
+    small = workloads.make_config(2, device="cuda", num_seqs=5, name="gqa_b5")
+    full = workloads.make_config(2, device="cuda")
+    rows_multi = workloads.build(workloads.Spec(
+        name="f32_prefill_rows", dtype="f32", num_seqs=6, q_heads=8, kv_heads=2,
+        head_dim=64, page_size=4, len_lo=1, len_hi=80, q_lo=1, q_hi=6, pool_factor=1.5),
+        5, device="cuda")
+    verify = workloads.make_config(2, device="cuda", num_seqs=16, q_lo=4, q_hi=4,
+                                   name="gqa_b16_q4")
+    window = workloads.make_config(3, device="cuda", num_seqs=6, name="window_b6")
+    # bounds at or above every context: the small batch takes more wavefronts with the
+    # table's full 4096 rows than with its own longest context
+    plan = [(tiny, None), (small, None), (small, 256 * 16), (full, None), (full, 256 * 16),
+            (rows_multi, None), (verify, None), (small, None), (window, None), (tiny, None),
+            (full, None)]
+    need = max(_need(sc, mc) for sc, mc in plan)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for sc, mc in plan:
+        out = _run_on_workspace(sc, ws, mc)
+        key = (sc.spec.name, mc)
+        if key in outs:
+            assert torch.equal(out, outs[key]), f"{key}: a repeated call differs"
+        outs[key] = out
+
+
+def test_workspace_reset_recovers_raised_counters():
+    """A workspace whose counters were left raised (as after a call that did not
+    complete) is usable again after pa_reset_workspace."""
+    sc = workloads.make_config(2, device="cuda")
+    ws = torch.zeros(_need(sc), dtype=torch.uint8, device="cuda")
+    first = _run_on_workspace(sc, ws)
+    ws[:4096] = 0x5A          # every counter raised
+    ops().reset_workspace(ws)
+    assert int(ws[:4096].count_nonzero()) == 0
+    assert torch.equal(_run_on_workspace(sc, ws), first)
 
 
 def test_deterministic_and_placement_invariant():
