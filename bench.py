@@ -162,28 +162,20 @@ def measured_traffic(path: str, workload: str):
         return None
 
 
-def pages_unshared(sc) -> bool:
-    """True when no physical page is attended by two sequences (block tables of pages of
-    16 rows or more; a raw slot table is not checked and gets no hint)."""
+def allocator_unshared(sc) -> bool:
+    """The allocator's answer to "is any page held twice?": the batch's tables are
+    registered in a ``PagedKVCache`` (each page named takes a reference) and it reports
+    whether every page has a single holder.  Raw slot tables get no hint (the decode
+    path that reads them does not use it)."""
+    from paged_kv_cache_41_amd.alloc import PagedKVCache
     s = sc.spec
-    if sc.table_page_size != s.page_size or s.page_size < 16:
+    if sc.table_page_size != s.page_size:
         return False
+    cache = PagedKVCache(sc.pool_pages, s.page_size)
     bt = sc.block_tables.cpu().numpy()
-    lens = sc.context_lens.cpu().numpy()
-    seen = set()
-    for b in range(len(lens)):
-        L = int(lens[b])
-        if L <= 0:
-            continue
-        lo = L - min(L, s.window) if s.window > 0 else 0
-        pages = set(range(lo // s.page_size, (L - 1) // s.page_size + 1))
-        if s.sinks > 0 and L > s.window:
-            pages |= set(range(0, (s.sinks - 1) // s.page_size + 1))
-        phys = {int(bt[b, j]) for j in pages}
-        if seen & phys:
-            return False
-        seen |= phys
-    return True
+    for b, L in enumerate(sc.lens.tolist()):
+        cache.adopt(b, bt[b], int(L), sinks=s.sinks)
+    return cache.unshared(range(len(sc.lens)))
 
 
 def copy_ceiling(dev, nbytes: int = 2 << 30, reps: int = 10) -> dict:
@@ -271,13 +263,76 @@ def table_update_timing(sc, dev, reps: int = 50) -> dict:
                     "kernel's own time"}
 
 
-def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
-    """The oracle, single-threaded, over whole sequences of the batch until ~budget_s."""
+# ---- CPU baseline: the oracle on a pool of worker processes ------------------------------
+# The pool is forked before this process touches the GPU, and the inputs reach the
+# workers through named shared memory once the GPU run has made them, so no worker is a
+# copy of a process holding a GPU context.  One BLAS thread per worker, one task per
+# sequence (or per sequence's query rows).
+_WORK = {}
+
+
+def _worker_init():
+    # one BLAS thread per worker, whether or not the parent had loaded BLAS before the fork
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401  (loads BLAS, so the limit below finds it)
+    from threadpoolctl import threadpool_limits
+    _WORK["limit"] = threadpool_limits(limits=1)
+
+
+def _worker_attach(desc):
+    """Map the shared arrays named in ``desc`` (once per worker and workload)."""
+    import numpy as np
+    from multiprocessing import resource_tracker, shared_memory
+    if _WORK.get("key") != desc["key"]:
+        arrays, handles = {}, []
+        for name, (shm_name, shape, dtype) in desc["arrays"].items():
+            h = shared_memory.SharedMemory(name=shm_name)
+            # the creating process owns (and unlinks) the segment: keep the tracker this
+            # attach registered it with from claiming it too
+            resource_tracker.unregister(h._name, "shared_memory")
+            handles.append(h)
+            arrays[name] = np.ndarray(shape, dtype=dtype, buffer=h.buf)
+        _WORK.update(key=desc["key"], arrays=arrays, handles=handles)
+    return _WORK["arrays"]
+
+
+def _worker_task(job):
+    desc, i = job
+    import oracle
+    a = _worker_attach(desc)
+    kw = desc["scalars"]
+    if "q_start" in a:
+        qs = a["q_start"]
+        oracle.attention.prefill(a["q"], a["k"], a["v"], a["bt"], a["ctx"], qs, kw["tps"],
+                                 kw["window"], kw["scale"], kw["dtype"],
+                                 rows=range(int(qs[i]), int(qs[i + 1])))
+    else:
+        oracle.attention.decode(a["q"], a["k"], a["v"], a["bt"], a["ctx"], kw["tps"],
+                                kw["window"], kw["scale"], kw["dtype"], seqs=[i],
+                                sinks=kw["sinks"])
+    return i
+
+
+def cpu_workers() -> int:
+    """Workers of the oracle pool: the cores this process may run on, at most 16 (the
+    host share of one GPU on the boxes this runs on)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def start_cpu_pool():
+    """Fork the worker pool; call before anything initialises the GPU."""
+    import multiprocessing as mp
+    return mp.get_context("fork").Pool(cpu_workers(), initializer=_worker_init)
+
+
+def cpu_baseline(sc, pool, budget_s: float = 3.0) -> dict:
+    """The oracle over the same batch on the pool: one warm-up pass, then three timed
+    runs, each as many whole passes over the batch as fit in ``budget_s`` seconds of
+    wall time; the median run's rate is reported."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
-
-    import oracle
+    from multiprocessing import shared_memory
 
     def bits(t):
         t = t.detach().cpu()
@@ -288,33 +343,51 @@ def cpu_baseline(sc, budget_s: float = 12.0) -> dict:
     tps = sc.table_page_size
     kp, vp = bits(sc.k_pool), bits(sc.v_pool)
     n_, P = kp.shape[:2]
-    kp = kp.reshape(n_ * P // tps, tps, *kp.shape[2:])
-    vp = vp.reshape(n_ * P // tps, tps, *vp.shape[2:])
-    q = bits(sc.q)
-    bt = sc.block_tables.cpu().numpy().astype(np.int64)
-    ctx = sc.context_lens.cpu().numpy().astype(np.int64)
-    elt = 4 if s.dtype == "f32" else 2
-    torch_threads = torch.get_num_threads()
-    torch.set_num_threads(1)
-    done, kv_bytes, t0 = 0, 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < budget_s:
-            i = done % s.num_seqs
-            if sc.q_start is not None:
-                qs = sc.q_start.cpu().numpy()
-                oracle.attention.prefill(q, kp, vp, bt, ctx, qs, tps, s.window, sc.scale, s.dtype,
-                                         rows=range(int(qs[i]), int(qs[i + 1])))
-            else:
-                oracle.attention.decode(q, kp, vp, bt, ctx, tps, s.window, sc.scale, s.dtype,
-                                        seqs=[i], sinks=s.sinks)
-            kv_bytes += int(2 * (sc.lens[i] - sc.lo[i]) * s.kv_heads * s.head_dim * elt)
-            done += 1
-    dt = time.perf_counter() - t0
-    torch.set_num_threads(torch_threads)
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seqs_per_s": round(done / dt, 3),
-            "sample": f"{done} sequences of this batch in order (cycling), fp64 gather + dense "
-                      f"attention, {dt:.1f} s on 1 thread"}
+    host = {"k": kp.reshape(n_ * P // tps, tps, *kp.shape[2:]),
+            "v": vp.reshape(n_ * P // tps, tps, *vp.shape[2:]),
+            "q": bits(sc.q), "bt": sc.block_tables.cpu().numpy().astype(np.int64),
+            "ctx": sc.context_lens.cpu().numpy().astype(np.int64)}
+    if sc.q_start is not None:
+        host["q_start"] = sc.q_start.cpu().numpy().astype(np.int64)
+    handles = []
+    try:
+        arrays = {}
+        for name, arr in host.items():
+            h = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+            handles.append(h)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=h.buf)[...] = arr
+            arrays[name] = (h.name, arr.shape, arr.dtype.str)
+        desc = {"key": f"{s.name}-{sc.seed}", "arrays": arrays,
+                "scalars": {"tps": tps, "window": s.window, "scale": sc.scale,
+                            "dtype": s.dtype, "sinks": s.sinks}}
+        B = s.num_seqs
+        jobs = [(desc, i) for i in range(B)]
+        elt = 4 if s.dtype == "f32" else 2
+        pass_bytes = int((2 * (sc.lens - sc.lo) * s.kv_heads * s.head_dim * elt).sum())
+        pool.map(_worker_task, jobs, chunksize=1)          # warm-up: attach, page in
+        rates = []
+        for _ in range(3):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                pool.map(_worker_task, jobs, chunksize=1)
+                passes += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            rates.append((passes * pass_bytes / dt, passes * B / dt, passes, dt))
+        rates.sort()
+        gbps, seqs, passes, dt = rates[1]
+    finally:
+        for h in handles:
+            h.close()
+            h.unlink()
+    n = cpu_workers()
+    return {"value": round(gbps / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "seqs_per_s": round(seqs, 3),
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": f"the whole batch ({B} sequences), {passes} passes in {dt:.1f} s (median "
+                      f"of 3 runs after a warm-up pass): fp64 gather + dense attention, one "
+                      f"task per sequence on {n} worker processes with one BLAS thread each"}
 
 
 def main():
@@ -330,6 +403,7 @@ def main():
     import workloads
     from paged_kv_cache_41_amd import ops
 
+    pool = None if args.no_cpu_baseline else start_cpu_pool()
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -376,9 +450,9 @@ def main():
     nb = decode_bytes(sc)
     kv_bytes_step = nb["kv"]
 
-    # the cache hint is passed only when, checked here on the host, no physical page is
-    # attended by two sequences of the batch
-    unshared = pages_unshared(sc)
+    # the cache hint is passed only when the allocator holding the batch's tables finds
+    # no page with two holders
+    unshared = allocator_unshared(sc)
 
     def step():
         ops.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
@@ -545,8 +619,8 @@ def main():
                              "every step starts after a 1 GiB write"),
                    "launch": ("each step one HIP graph replay (copy, store, attention)"
                               if args.graph else "kernels launched one by one"),
-                   "cache_hint": ("unshared pages (checked on the host): V rows read with the "
-                                  "non-temporal hint" if unshared and not multi else "none")},
+                   "cache_hint": ("unshared pages (the allocator's reference counts): V rows read "
+                                  "with the non-temporal hint" if unshared and not multi else "none")},
         "seqs_per_s": round(s.num_seqs / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * nb["kv"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "step": {"avg_us": round(float(step_ms.mean()) * 1e3, 2),
@@ -573,8 +647,10 @@ def main():
     result["memory"] = memory_report(sc)
     if not args.no_copy_ceiling:
         result["hbm_copy_reference"] = copy_ceiling(dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(sc)
+    if pool is not None:
+        result["cpu_baseline"] = cpu_baseline(sc, pool)
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
 
 
