@@ -61,7 +61,8 @@ enum pa_status {
   PA_EINVAL = -1,        /* a null pointer, a non-positive size, inconsistent sizes  */
   PA_EUNSUPPORTED = -2,  /* a valid combination this build has no kernel for         */
   PA_EWORKSPACE = -3,    /* decode workspace missing or smaller than required        */
-  PA_ELAUNCH = -4        /* the HIP runtime rejected a launch                         */
+  PA_ELAUNCH = -4,       /* the HIP runtime rejected a launch                         */
+  PA_ESCRATCH = -5       /* pa_decode_noalloc: the call needs more than its buffer    */
 };
 
 /* Human-readable name of a status code; never NULL. */
@@ -203,6 +204,32 @@ int pa_decode_hinted(float* out, const void* q, const void* k_pool, const void* 
                      int32_t window, int32_t sinks, int32_t hints, int32_t max_context_len,
                      float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
                      void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode_hinted with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, hosts that forbid allocation during a
+ * step).  The workspace is a buffer of PA_NOALLOC_SCRATCH_BYTES bytes held by
+ * the library in device memory: one per GPU the library runs on, kept until
+ * the process ends.  Its counter header is cleared by the first call on each
+ * device (a kernel on `stream`), and every completed call leaves it at zero.
+ *   Arguments, results and supported shapes are those of pa_decode_hinted;
+ *   the output is bit-identical to pa_decode_hinted with the same arguments.
+ *   Every call on a GPU uses that GPU's one buffer: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and give wrong
+ *   results; a call that does not complete leaves the buffer's counters
+ *   raised for every later call in the process.
+ *   Calls no hipMalloc, hipFree or other allocating routine.
+ * Errors: those of pa_decode_hinted; PA_ESCRATCH when the call would need
+ * more than PA_NOALLOC_SCRATCH_BYTES (nothing is launched).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pa_decode_noalloc(float* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t q_heads,
+                      int32_t kv_heads, int32_t head_dim, int32_t num_pages, int32_t page_size,
+                      int32_t window, int32_t sinks, int32_t hints, int32_t max_context_len,
+                      float scale, int32_t dtype, void* stream);
 
 /*
  * pa_prefill -- several query tokens per sequence against its cached rows: a

@@ -11,13 +11,14 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH, PA_ESCRATCH = 0, -1, -2, -3, -4, -5
 
 # every symbol include/pa.h declares, with its ctypes signature
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 PA_HINT_UNSHARED = 1
 PA_WORKSPACE_HEADER = 4096
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -36,6 +37,8 @@ SIGNATURES = {
                                   ctypes.POINTER(ctypes.c_size_t), _P]),
     "pa_update_tables": (ctypes.c_int, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
     "pa_reset_workspace": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+    "pa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                         _I, _I, _I, ctypes.c_float, _I, _P]),
 }
 
 _lib = None

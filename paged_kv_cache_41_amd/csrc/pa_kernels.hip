@@ -21,6 +21,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa.h"
 #include "pa_common.hpp"
 #include "pa_decode_mfma.hpp"
@@ -391,6 +393,7 @@ extern "C" const char* pa_status_string(int status) {
     case PA_EUNSUPPORTED: return "unsupported combination";
     case PA_EWORKSPACE: return "workspace missing or too small";
     case PA_ELAUNCH: return "kernel launch failed";
+    case PA_ESCRATCH: return "the call needs more scratch than the no-allocation buffer holds";
     default: return "unknown status";
   }
 }
@@ -743,6 +746,68 @@ extern "C" int pa_reset_workspace(void* workspace, size_t workspace_bytes, void*
                      reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<unsigned char*>(workspace), n);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+// ------------------------------------------------------------------------------------
+// No-allocation decode: the workspace is a file-scope device array.  Each GPU the library
+// runs on holds its own copy (at its own address) until the process ends.  Host code
+// never passes the array's name to a kernel: on the host that name is a stand-in, not a
+// device address.  The address is taken once per device with hipGetSymbolAddress, with
+// that device current, and kept here.
+// ------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];       // device address of `scratch`, per device ordinal
+bool scratch_zeroed[kMaxDevices];     // its counter header has been cleared once
+
+// This device's scratch, its counter header cleared on first use (stream-ordered before
+// the caller's kernels; every completed call leaves the counters at zero after that).
+int device_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return PA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ELAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  if (!scratch_zeroed[dev]) {
+    hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(256), 0, st,
+                       reinterpret_cast<unsigned char*>(scratch_ptr[dev]), (int)WS_HEADER);
+    if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+    scratch_zeroed[dev] = true;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
+}
+}  // namespace
+
+extern "C" int pa_decode_noalloc(float* out, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 int32_t bt_stride, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t num_pages, int32_t page_size,
+                                 int32_t window, int32_t sinks, int32_t hints,
+                                 int32_t max_context_len, float scale, int32_t dtype,
+                                 void* stream) {
+  // the size this call's path needs (validates every host-visible argument, no HIP call)
+  size_t need = 0;
+  int rc = decode_entry(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens, num_seqs,
+                        q_heads, kv_heads, head_dim, num_pages, page_size, window, sinks, hints,
+                        max_context_len, scale, dtype, nullptr, &need, stream);
+  if (rc != PA_OK) return rc;
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ESCRATCH;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = device_scratch(st, &ws)) != PA_OK) return rc;
+  size_t have = PA_NOALLOC_SCRATCH_BYTES;
+  return decode_entry(out, q, k_pool, v_pool, block_tables, bt_stride, context_lens, num_seqs,
+                      q_heads, kv_heads, head_dim, num_pages, page_size, window, sinks, hints,
+                      max_context_len, scale, dtype, ws, &have, stream);
 }
 
 extern "C" int pa_update_tables(int32_t* block_tables, int32_t bt_stride, int32_t bt_rows,

@@ -167,6 +167,34 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     return out
 
 
+def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, *, out: torch.Tensor,
+                   window: int = 0, sinks: int = 0, scale: Optional[float] = None,
+                   max_context_len: int = 0, stream=None, unshared_pages: bool = False) -> torch.Tensor:
+    """``decode`` through ``pa_decode_noalloc``: no workspace, nothing allocated (the
+    caller passes ``out``).  The library's one scratch buffer per GPU serves every such
+    call, so calls that overlap on one GPU race."""
+    dev = _dev(q, k_pool, v_pool, block_tables, context_lens, out)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_seqs, q_heads, head_dim] in the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] < B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [>= num_seqs, stride], context_lens [num_seqs]")
+    if out.shape != (B, hq, d) or out.dtype != torch.float32:
+        raise ValueError("out must be a contiguous fp32 [num_seqs, q_heads, head_dim]")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if scale is None:
+        scale = d ** -0.5
+    lib = _lib.load()
+    _lib.check("pa_decode_noalloc", lib.pa_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), B, hq, hkv,
+        d, n, P, int(window), int(sinks), _lib.PA_HINT_UNSHARED if unshared_pages else 0,
+        int(max_context_len), float(scale), _code(q), _stream(dev, stream)))
+    return out
+
+
 def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
                   window, scale, max_context_len, ws_ptr, ws_size, stream_handle):
     n, P, hkv, d = _pool_dims(k_pool, v_pool)
