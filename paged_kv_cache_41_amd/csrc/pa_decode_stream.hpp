@@ -11,12 +11,12 @@
 //
 // Every workgroup first turns the context lengths into per-sequence tile counts and an
 // exclusive prefix sum in LDS.  Each wavefront then runs a three-stage software pipeline
-// over its tiles: the block-table entry of tile i+3 (one per tile, read through the scalar
-// unit, for pages of at least 16 rows; one per lane for smaller pages), the K and V rows
-// of tile i+2, and the compute of tile i.  All loads are unconditional: a row outside the
-// attended range or behind an unmapped entry is read from a clamped address inside the
-// pool and masked out of the softmax and P.V; past the end of the range the last tile
-// is re-read (a cache hit).
+// over its tiles: the block-table entry of tile i+D+1 (one per tile, read through the
+// scalar unit, for pages of at least 16 rows; one per lane for smaller pages), the K and V
+// rows of tile i+D, and the compute of tile i (D = STREAM_DEPTH tiles in flight).  All
+// loads are unconditional: a row outside the attended range or behind an unmapped entry is
+// read from a clamped address inside the pool and masked out of the softmax and P.V; past
+// the end of the range the last tile is re-read (a cache hit).
 //
 // Compute per tile runs on the matrix cores twice.  Scores: four
 // v_mfma_f32_16x16x32_bf16 with the K tile as the A operand (row = token; the sum over
@@ -72,7 +72,9 @@ constexpr int BMAX = 2048;      // sequences handled by this path
 constexpr float RESCALE_T = 8.f;
 constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
 #ifndef STREAM_DEPTH
-#define STREAM_DEPTH 2   // tiles of K/V in flight per wavefront while one is computed
+#define STREAM_DEPTH 1   // tiles of K/V in flight per wavefront while one is computed (two
+                         // measured 1-1.7 us slower on the batch-64 and window workloads:
+                         // more bytes in flight per compute unit only lengthen the queues)
 #endif
 #ifndef STREAM_MULTI_DEPTH
 #define STREAM_MULTI_DEPTH 1   // the same with several query tokens per sequence (its
