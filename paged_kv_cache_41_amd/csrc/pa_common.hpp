@@ -33,6 +33,8 @@ struct DecodeArgs {
   float* ws_acc;               // partial accumulators, head_dim floats each
   int* ws_arrive;              // streaming path: per-range arrival counters, zero between calls
   int total_waves;             // streaming path: wavefronts sharing the tile list
+  int try_aligned;             // streaming path, one query token: launch the kernel that gives
+                               // each workgroup whole segments when they are even
   // Several query tokens per sequence (prefill chunk, verify step).  Streaming path: the
   // query rows of sequence s are q_start[s] .. q_start[s+1]-1 of q and out (num_q rows,
   // at most max_q per sequence).  Other paths: every query row is a row of its own, with

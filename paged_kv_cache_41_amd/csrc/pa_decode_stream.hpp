@@ -154,6 +154,35 @@ __device__ __forceinline__ int range_of(int T, int R, int x) {
   return (int)(((int64_t)(x + 1) * R - 1) / T);
 }
 
+// Aligned partition (single-query decode): when the segments are about equal, each
+// workgroup takes an equal count of whole segments (its first tile in st_wgb), and its four
+// wavefronts split that range in equal parts.  No segment then crosses a workgroup, and the pieces of a cut segment are
+// combined through LDS after a workgroup barrier, with no device-scope exchange.
+__shared__ int st_wgb[BMAX / 4 + 1];
+// partial (max and sum of every column, then the accumulators) of each wavefront's first
+// and last segment piece, in the aligned partition
+__shared__ float st_part[NW][2][16 * (2 + HD)];
+struct Part {
+  bool aligned;
+  int T, R;        // flat: R equal ranges of the T tiles
+  __device__ __forceinline__ int start(int r) const {
+    if (!aligned) return range_start(T, R, r);
+    const int g = r >> 2, q = r & 3, A = st_wgb[g];
+    return q == 0 ? A : A + (int)((int64_t)q * (st_wgb[g + 1] - A) / 4);   // (r = R: g = NWG)
+  }
+  __device__ __forceinline__ int of(int x) const {
+    if (!aligned) return range_of(T, R, x);
+    int lo = 0, hi = R / 4 - 1;   // the workgroup whose range holds x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (st_wgb[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    int r = 4 * lo + 3;
+    while (start(r) > x) --r;
+    return r;
+  }
+};
+
 // What the load and compute stages need of one tile.
 enum : int {
   RANGE_FIRST = 1,   // first tile of the range
@@ -301,7 +330,7 @@ struct Front {
 // columns share every K/V tile a wavefront loads.
 // VNT: the V rows are loaded with the non-temporal cache hint (pages not shared, so no
 // reuse to keep); K keeps the default policy, since its four loads per row share lines.
-template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false>
+template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false, bool ALIGN = false>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   constexpr bool MULTI = NB > 0;
   constexpr int NBX = MULTI ? NB : 1;
@@ -414,13 +443,37 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   }
   }
 
-  // ---- this wavefront's range ------------------------------------------------------------
+  // ---- the partition and this wavefront's range ----------------------------------------
   const int T = uni(Hkv * st_cum[B]);
-  const int R = min(a.total_waves, T);
+  Part part_of{false, T, min(a.total_waves, T)};
+  if constexpr (!MULTI && ALIGN) {
+    // Aligned partition: workgroup g takes segments g NSEG / NWG to (g + 1) NSEG / NWG - 1
+    // (NSEG = B Hkv, split by count: even segments give even workgroups, with no drift);
+    // it is used when no workgroup then holds more than 1/16 above the mean.  Every
+    // workgroup computes the same split, so all take the same decision.  The tile list
+    // holds the kv heads of sequence s one after the other from Hkv st_cum[s] on, each
+    // with st_cum[s + 1] - st_cum[s] tiles.
+    const int NWG = gridDim.x;
+    if (NWG * NW == a.total_waves && NWG <= BMAX / 4 && T >= NWG) {
+      if (tid == 0) st_scan[0] = 0;
+      for (int g = tid; g <= NWG; g += 64 * NW) {
+        const int j = (int)((int64_t)g * B * Hkv / NWG);
+        const int sq = j / Hkv, h = j - sq * Hkv;
+        st_wgb[g] = sq >= B ? T : Hkv * st_cum[sq] + h * (st_cum[sq + 1] - st_cum[sq]);
+      }
+      __syncthreads();
+      if (tid < NWG) atomicMax(&st_scan[0], st_wgb[tid + 1] - st_wgb[tid]);
+      __syncthreads();
+      const int mean = (T + NWG - 1) / NWG;
+      part_of.aligned = st_scan[0] <= mean + mean / 16;
+      if (part_of.aligned) part_of.R = a.total_waves;
+    }
+  }
+  const int R = part_of.R;
   const int kw = blockIdx.x * NW + w;
-  if (kw >= R) return;
-  const int ta = range_start(T, R, kw);
-  const int n = range_start(T, R, kw + 1) - ta;
+  if (!part_of.aligned && kw >= R) return;
+  const int ta = part_of.start(kw);
+  const int n = part_of.start(kw + 1) - ta;
 
   const int P = a.page_size;
   const int lp = 31 - __clz(P);
@@ -437,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   fr.Hkv = Hkv;
   fr.window = a.window;
   fr.sinks = a.sinks;
-  fr.locate(ta);
+  if (n > 0) fr.locate(ta);   // (an aligned range may be empty)
   fr.rem = n;
   fr.first = true;
   fr.idle = false;
@@ -641,6 +694,22 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
             o[1] = make_float4(ac[4][r] * inv, ac[5][r] * inv, ac[6][r] * inv, ac[7][r] * inv);
           }
         }
+      } else if (!MULTI && part_of.aligned) {
+        // aligned partition: the piece's partial stays in LDS for the workgroup's combine
+        float* pl = st_part[w][first_seg ? 0 : 1];
+        if (lane < C) {
+          pl[2 * lane] = m_ref[i];
+          pl[2 * lane + 1] = lt;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * grp + r;
+          if (h < C) {
+            float* pa = pl + 2 * C + h * HD + col * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pa[e] = oacc[i][e][r];
+          }
+        }
       } else {
         const int c0 = i * 16;
         if (lane < min(C - c0, 16))
@@ -660,7 +729,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     if (!complete) {
       const int tiles = st_cum[d.s + 1] - st_cum[d.s];
       const int seg_start = Hkv * st_cum[d.s] + d.g * tiles;
-      const int k1 = range_of(T, R, seg_start), k2 = range_of(T, R, seg_start + tiles - 1);
+      const int k1 = part_of.of(seg_start), k2 = part_of.of(seg_start + tiles - 1);
       if (first_seg) {
         cut0 = true;
         seg0 = d.s * Hkv + d.g;
@@ -788,6 +857,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // is re-read (a cache hit) and skipped.
   Tile buf[DEPTH + 1];
   Desc dsc[DEPTH + 1];
+  if (n > 0) {
   Desc d_next = fr.desc();
   int e_next = table_entry(d_next);
   fr.next();
@@ -815,34 +885,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     }
     if (uni(dsc[DEPTH].flags) & IDLE) break;
   }
-
-  // ---- cut segments: the piece that arrives last combines them ---------------------------
-  // Each piece counts itself on the counter of the segment's first range once its partial
-  // is written; the one that completes the count reads every piece's partial, combines
-  // them in range order, and puts the counter back to zero for the next call.  Partials
-  // and counters move only through device-scope accesses (stores written through, loads
-  // that skip the caches of the compute unit and of its die), and the count is raised only
-  // after this wavefront's partial stores have completed (vmcnt reaches 0), so a
-  // wavefront that sees the full count reads complete partials.  No cache-wide write-back
-  // or invalidate is needed: nothing is exchanged through ordinary cached stores.
-  if (!cut0 && !cut1) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);   // all counters: every store above has completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int arrived0 = 0, arrived1 = 0;
-  if (lane == 0) {
-    if (cut0)
-      arrived0 = __hip_atomic_fetch_add(a.ws_arrive + k1_0, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    if (cut1)
-      arrived1 = __hip_atomic_fetch_add(a.ws_arrive + k1_1, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  arrived0 = __builtin_amdgcn_readlane(arrived0, 0);
-  arrived1 = __builtin_amdgcn_readlane(arrived1, 0);
-  const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
-  const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
-  if (!last0 && !last1) return;
+
   // One wavefront combines a segment, CPP columns per pass: lane l of the NL lanes doing
   // it takes head_dim QPL floats of column l / LPC (+ CPP per pass), LPC = NL / CPP; the
   // partials of COMBINE_BATCH pieces are loaded together.  Decode (at most 16 columns,
@@ -858,7 +902,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     const int tiles = st_cum[s + 1] - st_cum[s];
     const int seg_start = Hkv * st_cum[s] + g * tiles;
     // in range k1 the segment is the first one (slot 0) only if it starts the range
-    const int slot1 = seg_start == range_start(T, R, k1) ? 0 : 1;
+    const int slot1 = seg_start == part_of.start(k1) ? 0 : 1;
     float* out = a.out + ((size_t)s * a.q_heads + (size_t)g * G) * HD;
     int ncols = G;
     if constexpr (MULTI) {
@@ -877,6 +921,16 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
+          if (!MULTI && part_of.aligned) {
+            // the piece of wavefront k - NW blockIdx of this workgroup, from LDS
+            const float* pl = st_part[k - (int)blockIdx.x * NW][k == k1 ? slot1 : 0];
+            ml[b] = make_float2(pl[2 * h], pl[2 * h + 1]);
+            const float* src = pl + 2 * C + h * HD + cd;
+#pragma unroll
+            for (int q = 0; q < QPL; ++q)
+              x[b][q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+            continue;
+          }
           const size_t pi = (size_t)k * 2 + (k == k1 ? slot1 : 0);
           ml[b] = part.load2(ml_off((uint32_t)pi * C + h));
           const uint32_t o = acc_off((uint32_t)pi * C + h) + cd * 4;
@@ -907,9 +961,60 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       for (int q = 0; q < QPL; ++q)
         o[q] = make_float4(nm[q].x * inv, nm[q].y * inv, nm[q].z * inv, nm[q].w * inv);
     }
-    if (sl == 0)
+    if (sl == 0 && !(!MULTI && part_of.aligned))
       __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+  // ---- cut segments: the piece that arrives last combines them ---------------------------
+  // Each piece counts itself on the counter of the segment's first range once its partial
+  // is written; the one that completes the count reads every piece's partial, combines
+  // them in range order, and puts the counter back to zero for the next call.  Partials
+  // and counters move only through device-scope accesses (stores written through, loads
+  // that skip the caches of the compute unit and of its die), and the count is raised only
+  // after this wavefront's partial stores have completed (vmcnt reaches 0), so a
+  // wavefront that sees the full count reads complete partials.  No cache-wide write-back
+  // or invalidate is needed: nothing is exchanged through ordinary cached stores.
+  if constexpr (!MULTI) {
+    if (part_of.aligned) {
+      // every piece of a cut segment lies in this workgroup: after the barrier the wavefront
+      // holding a segment's first piece combines it from LDS.  A workgroup with fewer tiles
+      // than wavefronts has empty ranges, which can lie between a segment's first and last
+      // pieces: they publish a running max of -inf, a piece the combine skips.
+      if (n == 0 && lane < C) {
+        st_part[w][0][2 * lane] = -INFINITY;
+        st_part[w][1][2 * lane] = -INFINITY;
+      }
+      __syncthreads();
+      const bool own0 = cut0 && k1_0 == kw, own1 = cut1 && k1_1 == kw;
+      if (own0 && own1) {
+        const bool hi = lane >= 32;
+        combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0,
+                hi ? k1_1 : k1_0, hi ? k2_1 : k2_0);
+      } else if (own0) {
+        combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
+      } else if (own1) {
+        combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
+      }
+      return;
+    }
+  }
+  if (!cut0 && !cut1) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: every store above has completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int arrived0 = 0, arrived1 = 0;
+  if (lane == 0) {
+    if (cut0)
+      arrived0 = __hip_atomic_fetch_add(a.ws_arrive + k1_0, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    if (cut1)
+      arrived1 = __hip_atomic_fetch_add(a.ws_arrive + k1_1, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+  }
+  arrived0 = __builtin_amdgcn_readlane(arrived0, 0);
+  arrived1 = __builtin_amdgcn_readlane(arrived1, 0);
+  const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
+  const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
+  if (!last0 && !last1) return;
   if constexpr (!MULTI) {
     if (last0 && last1) {
       const bool hi = lane >= 32;
@@ -978,15 +1083,27 @@ inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
   a.ws_acc = a.ws_ml + slots * 2;
 }
 
-template <int NB>
-inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
+template <int NB, bool ALIGN>
+inline void launch_variant(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
   constexpr int D = NB > 0 ? STREAM_MULTI_DEPTH : STREAM_DEPTH;
   if (a.page_size >= TILE && (a.hints & PA_HINT_UNSHARED))
-    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true, ALIGN>), grid, block, 0, st, a);
   else if (a.page_size >= TILE)
-    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, false, ALIGN>), grid, block, 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, false, ALIGN>), grid, block, 0, st,
+                       a);
+}
+
+// Only a kernel built with ALIGN tries the aligned partition, so the others carry none of
+// its branches.
+template <int NB>
+inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
+  if (NB == 0 && a.try_aligned)
+    launch_variant<NB, NB == 0>(a, st, grid, block);
+  else
+    launch_variant<NB, false>(a, st, grid, block);
 }
 
 // nb = 0: one query token per sequence; 1 or 2: blocks per group of query tokens

@@ -497,6 +497,17 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
+    // With a window every segment holds at most window / 16 + 1 tiles, so segments are
+    // often about equal: a grid of ceil(segs / k) workgroups, k = ceil(segs / 256), gives
+    // each workgroup k or k - 1 whole segments, which lets the kernel use its aligned
+    // partition (pieces of a cut segment combined in LDS) when the segments are even
+    const int64_t segs = (int64_t)num_seqs * kv_heads;
+    if (window > 0 && window < max_context_len && segs >= 64) {
+      const int64_t wg_max = stream_waves_max / stream::NW;
+      const int64_t k = (segs + wg_max - 1) / wg_max;
+      waves = stream::NW * ((segs + k - 1) / k);
+      a.try_aligned = 1;
+    }
     const size_t need = stream::workspace_bytes((int)waves, group);
     if (!workspace) {
       *workspace_bytes = need;

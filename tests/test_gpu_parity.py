@@ -133,6 +133,46 @@ def test_config_slot_table_full():
     check_step(sc)
 
 
+# (sequences, kv heads, window, sinks, context lengths low and high, empty sequences)
+ALIGNED_CASES = {
+    # every segment 64 or 65 tiles, one per workgroup
+    "one_segment_per_workgroup": (64, 4, 1024, 0, 1024, 3000, 0),
+    # a few empty sequences: some workgroups get no tiles and only join the barrier
+    "empty_workgroups": (64, 4, 1024, 0, 1024, 3000, 3),
+    # 2048 segments of 16 or 17 tiles, eight per workgroup
+    "eight_segments_per_workgroup": (256, 8, 256, 0, 300, 900, 0),
+    # segments of 2 or 3 tiles: wavefronts with no tile between the pieces of a segment
+    "short_segments": (64, 4, 32, 0, 40, 200, 0),
+    # sink rows: a tile of their own ahead of every window
+    "sinks": (64, 4, 1024, 4, 1100, 3000, 0),
+    # contexts mostly inside the window: segments too uneven, the flat split is kept
+    "uneven_keeps_flat_split": (64, 4, 1024, 0, 16, 2000, 0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ALIGNED_CASES))
+def test_window_segments_aligned_to_workgroups(case):
+    """With a window, the host sizes the grid so that each workgroup can take whole
+    segments; when they are about equal the kernel does so and combines the pieces of a
+    cut segment in LDS, else it keeps the equal flat split.  Either way the result is the
+    oracle's."""
+    B, hkv, window, sinks, lo, hi, empty = ALIGNED_CASES[case]
+    lens = np.random.default_rng(40 + B + window + sinks + lo).integers(lo, hi, size=B)
+    lens[:empty] = 0
+    spec = workloads.Spec(name=f"window_aligned_{case}", dtype="bf16", num_seqs=B,
+                          q_heads=4 * hkv, kv_heads=hkv, head_dim=128, page_size=16,
+                          window=window, sinks=sinks, lens=tuple(int(x) for x in lens),
+                          pool_factor=1.25, spare="nan")
+    sc = workloads.build(spec, 44 + empty, device="cuda")
+    # the flat split leaves partials of cut segments past the counter header; the aligned
+    # one keeps them in LDS and writes nothing there
+    ws = torch.zeros(_need(sc), dtype=torch.uint8, device="cuda")
+    ws[4096:] = 0x5A
+    _run_on_workspace(sc, ws)
+    untouched = bool((ws[4096:] == 0x5A).all())
+    assert untouched == (case != "uneven_keeps_flat_split"), case
+
+
 @pytest.mark.parametrize("window", [0, 40])
 def test_batch_above_streaming_limit(window):
     # more sequences than the streaming path takes: the chunked matrix-core path
