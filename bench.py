@@ -53,6 +53,12 @@ def parse():
                    help="before each step (outside the events) read (clean eviction) or "
                         "overwrite a 1 GiB buffer, so no K/V row is still in the 256 MB "
                         "last-level cache")
+    p.add_argument("--layout", choices=["token", "head"], default="token",
+                   help="pool layout: token-major [pages, page_size, kv_heads, head_dim] "
+                        "(default) or head-major [pages, kv_heads, page_size, head_dim]")
+    p.add_argument("--no-layout-compare", action="store_true",
+                   help="skip timing the same calls on head-major copies of the pools after "
+                        "the timed steps (a profile then holds one layout only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="replay the step as a HIP graph (measured slower than launching the "
@@ -144,9 +150,9 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path: str, workload: str):
+def measured_traffic(path: str, workload: str, layout: str = "token"):
     """HBM bytes per decode call from a committed counter summary, if it covers this
-    workload and was taken on the current kernel sources; else None."""
+    workload and pool layout and was taken on the current kernel sources; else None."""
     if not path or not os.path.exists(path) or workload != "gqa_b64":
         return None
     vals = {}
@@ -156,10 +162,43 @@ def measured_traffic(path: str, workload: str):
             vals[k.strip()] = v.strip()
     if vals.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
+    if vals.get("pool_layout", "token") != layout:
+        return None
     try:
         return int(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def head_major_timing(sc, attend_on, do_flush, stream, steps, nb):
+    """The timed attention calls again, cold, on head-major copies of the pools
+    (PA_HEAD_MAJOR, [pages, kv_heads, page_size, head_dim]) holding the same rows: the
+    result is bit-identical, only where each row sits in its page differs."""
+    import numpy as np
+    import torch
+    hk = sc.k_pool.transpose(1, 2).contiguous()
+    hv = sc.v_pool.transpose(1, 2).contiguous()
+    attend_on(hk, hv, "head")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        do_flush()
+        ev[i][0].record(stream)
+        attend_on(hk, hv, "head")
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    avg = float(ms.mean())
+    del hk, hv
+    return {"pool_layout": "head-major [pages, kv_heads, page_size, head_dim]",
+            "decode_avg_us": round(avg * 1e3, 2),
+            "decode_median_us": round(float(np.median(ms)) * 1e3, 2),
+            "kv_gbps": round(nb["kv"] / (avg * 1e-3) / 1e9, 1),
+            "achieved_gbps": round(nb["total"] / (avg * 1e-3) / 1e9, 1),
+            "frac": round(nb["total"] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "the same cold calls as `decode`, after the timed steps, on head-major "
+                    "copies of the pools; the headline uses the token-major layout"}
 
 
 def allocator_unshared(sc) -> bool:
@@ -424,6 +463,16 @@ def main():
     hkv, d = s.kv_heads, s.head_dim
     kv_view = (sc.k_pool, sc.v_pool) if sc.table_page_size == s.page_size else (
         sc.k_pool.view(-1, 1, hkv, d), sc.v_pool.view(-1, 1, hkv, d))
+    layout = args.layout
+    pools = (sc.k_pool, sc.v_pool)
+    if layout == "head":
+        if sc.table_page_size != s.page_size:
+            print("a raw slot table addresses pools viewed as pages of one row, which needs "
+                  "the token-major layout", file=sys.stderr)
+            sys.exit(2)
+        # the same rows, head-major; the oracle baseline keeps reading the token-major pools
+        pools = (sc.k_pool.transpose(1, 2).contiguous(), sc.v_pool.transpose(1, 2).contiguous())
+        kv_view = pools
     out = torch.empty(len(sc.q), s.q_heads, d, dtype=torch.float32, device=dev)
     multi = sc.q_start is not None
     max_q = max(int(sc.nq.max()), 1) if multi else 1
@@ -431,11 +480,11 @@ def main():
         need = ops.prefill_workspace_bytes(sc.q, sc.q_start, kv_view[0], kv_view[1],
                                            sc.block_tables, sc.context_lens, max_q_len=max_q,
                                            window=s.window, scale=sc.scale,
-                                           max_context_len=sc.max_context_len)
+                                           max_context_len=sc.max_context_len, layout=layout)
     else:
         need = ops.decode_workspace_bytes(sc.q, kv_view[0], kv_view[1], sc.block_tables,
                                           sc.context_lens, window=s.window, sinks=s.sinks,
-                                          max_context_len=sc.max_context_len)
+                                          max_context_len=sc.max_context_len, layout=layout)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     flush = None
     if args.flush != "none":
@@ -455,21 +504,27 @@ def main():
     unshared = allocator_unshared(sc)
 
     def step():
-        ops.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
-        ops.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+        ops.copy_pages(pools[0], pools[1], sc.copy_src, sc.copy_dst, layout=layout)
+        ops.store_kv(pools[0], pools[1], sc.k_new, sc.v_new, sc.slot_mapping, layout=layout)
+
+    def attend_on(kp, vp, lay):
+        if multi:
+            ops.prefill(sc.q, sc.q_start, kp, vp, sc.block_tables, sc.context_lens,
+                        max_q_len=max_q, window=s.window, scale=sc.scale,
+                        max_context_len=sc.max_context_len, out=out, workspace=ws, layout=lay)
+        else:
+            ops.decode(sc.q, kp, vp, sc.block_tables, sc.context_lens, window=s.window,
+                       sinks=s.sinks, scale=sc.scale, max_context_len=sc.max_context_len,
+                       out=out, workspace=ws, unshared_pages=unshared, layout=lay)
 
     def attend():
-        if multi:
-            ops.prefill(sc.q, sc.q_start, kv_view[0], kv_view[1], sc.block_tables,
-                        sc.context_lens, max_q_len=max_q, window=s.window, scale=sc.scale,
-                        max_context_len=sc.max_context_len, out=out, workspace=ws)
-        else:
-            ops.decode(sc.q, kv_view[0], kv_view[1], sc.block_tables, sc.context_lens,
-                       window=s.window, sinks=s.sinks, scale=sc.scale,
-                       max_context_len=sc.max_context_len, out=out, workspace=ws,
-                       unshared_pages=unshared)
+        attend_on(kv_view[0], kv_view[1], layout)
 
+    # warm-up steps start cold as the timed ones do, so that a profile of a run with
+    # --warm-steps 0 holds cold calls only
     for _ in range(args.warmup):
+        if flush is not None:
+            do_flush()
         step()
         attend()
     torch.cuda.synchronize()
@@ -564,7 +619,7 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     dec_avg = float(dec_ms.mean())
     achieved = nb["total"] / (dec_avg * 1e-3) / 1e9
-    traffic = measured_traffic(args.traffic, s.name)
+    traffic = measured_traffic(args.traffic, s.name, layout)
     flops = attention_flops(sc)
     G = s.q_heads // s.kv_heads
     streaming = (s.dtype == "bf16" and s.head_dim == 128 and G <= 16 and
@@ -617,6 +672,9 @@ def main():
                             if args.flush == "read" else
                             ("back-to-back steps" if args.flush == "none" else
                              "every step starts after a 1 GiB write"),
+                   "pool_layout": ("head-major [pages, kv_heads, page_size, head_dim]"
+                                   if layout == "head" else
+                                   "token-major [pages, page_size, kv_heads, head_dim]"),
                    "launch": ("each step one HIP graph replay (copy, store, attention)"
                               if args.graph else "kernels launched one by one"),
                    "cache_hint": ("unshared pages (the allocator's reference counts): V rows read "
@@ -641,6 +699,10 @@ def main():
         result["decode"]["tflops"] = round(flops / (dec_avg * 1e-3) / 1e12, 2)
     if warm is not None:
         result["warm_back_to_back"] = warm
+    if (layout == "token" and not args.no_layout_compare and flush is not None and
+            sc.table_page_size == s.page_size):
+        result["head_major_layout"] = head_major_timing(sc, attend_on, do_flush, stream,
+                                                        args.steps, nb)
     if s.prefix_len:
         result["config"]["unique_kv_bytes"] = unique_kv_bytes(sc)
     result["table_update"] = table_update_timing(sc, dev)

@@ -24,12 +24,15 @@
  *
  * Common conventions
  *   - Pools: one K pool and one V pool, each [num_pages, page_size, kv_heads,
- *     head_dim], row-major, of element type `dtype`.  A "slot" is a row of the
- *     flattened view [num_pages * page_size, kv_heads, head_dim]:
- *     slot = page * page_size + offset.  For more than one layer, pass each
- *     layer's base pointers.
+ *     head_dim] (token-major, the layout of the KV buffer in mini-sglang part 4),
+ *     row-major, of element type `dtype`; or head-major, [num_pages, kv_heads,
+ *     page_size, head_dim], when the dtype argument carries PA_HEAD_MAJOR.  A
+ *     "slot" is page * page_size + offset in both; with token-major pools it is a
+ *     row of the flattened view [num_pages * page_size, kv_heads, head_dim].  For
+ *     more than one layer, pass each layer's base pointers.
  *   - dtype: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16, upper half of a
- *     binary32).  q, new rows and pools share one dtype; decode output is fp32.
+ *     binary32), optionally OR-ed with PA_HEAD_MAJOR (see below).  q, new rows
+ *     and pools share one element type; decode output is fp32.
  *   - Every pointer argument is caller-owned device memory unless stated.
  *     The library allocates nothing, keeps no state between calls, never
  *     synchronizes, and enqueues all work on `stream` (a hipStream_t; NULL is
@@ -55,6 +58,19 @@ extern "C" {
 #endif
 
 enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 };
+
+/*
+ * Pool layout flag, OR-ed into the dtype argument of every call that takes the
+ * pools: they are head-major, [num_pages, kv_heads, page_size, head_dim].  A
+ * page holds page_size * kv_heads * head_dim elements in either layout, so
+ * slots, block tables and page copies do not change; only where a (token,
+ * kv head) row sits inside its page does.  Head-major puts the rows of one kv
+ * head in one contiguous block per page, so an attention pass over one head
+ * reads whole blocks instead of one head_dim slice of every token row.  With
+ * page_size 1 both layouts are the same bytes.  Every result is bit-identical
+ * to the same call on the token-major pool holding the same rows.
+ */
+#define PA_HEAD_MAJOR 0x100
 
 enum pa_status {
   PA_OK = 0,
@@ -98,13 +114,18 @@ int pa_reset_workspace(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_store_kv -- write new K/V rows into their slots.
- *   k_pool, v_pool  [num_pages, page_size, kv_heads, head_dim], written in place.
+ *   k_pool, v_pool  [num_pages, page_size, kv_heads, head_dim] (with
+ *                   PA_HEAD_MAJOR: [num_pages, kv_heads, page_size, head_dim]),
+ *                   written in place.
  *   k_new, v_new    [num_tokens, kv_heads, head_dim], contiguous.
  *   slot_mapping    device int32 [num_tokens]: flat slot of each row; a negative
  *                   slot skips that row.  Slots must be distinct within a call
  *                   (two rows for one slot: unspecified which one lands).
  * Every element of each row is copied bit for bit; no other byte of the pools
  * changes.  num_tokens == 0 is a no-op.
+ * Errors: PA_EINVAL for a non-positive size or an unknown dtype or flag;
+ * PA_EUNSUPPORTED when a row (token-major) or a head's row (head-major) is not
+ * a multiple of 4 bytes.
  */
 int pa_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_pages,

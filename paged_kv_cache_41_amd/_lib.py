@@ -17,6 +17,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH, PA_ESCRATCH = 0, -
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 PA_HINT_UNSHARED = 1
+PA_HEAD_MAJOR = 0x100   # pool layout flag OR-ed into the dtype argument
 PA_WORKSPACE_HEADER = 4096
 PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 

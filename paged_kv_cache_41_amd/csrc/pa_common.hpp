@@ -33,6 +33,11 @@ struct DecodeArgs {
   float* ws_acc;               // partial accumulators, head_dim floats each
   int* ws_arrive;              // streaming path: per-range arrival counters, zero between calls
   int total_waves;             // streaming path: wavefronts sharing the tile list
+  // Pool strides in elements of a token row and of a kv head within a page: token-major
+  // pool [pages, page_size, kv_heads, head_dim]: kv_heads * head_dim and head_dim;
+  // head-major [pages, kv_heads, page_size, head_dim]: head_dim and page_size * head_dim.
+  // A page is page_size * kv_heads * head_dim elements in both.
+  int row_stride, head_stride;
   int try_aligned;             // streaming path, one query token: launch the kernel that gives
                                // each workgroup whole segments when they are even
   // Several query tokens per sequence (prefill chunk, verify step).  Streaming path: the
@@ -44,6 +49,21 @@ struct DecodeArgs {
   int hints;                   // PA_HINT_* bits of the decode call (0: none)
   const int32_t* row_seq;      // nullptr: row s reads the table row of sequence s
 };
+
+// The dtype argument of a call that takes a pool: the element type, with PA_HEAD_MAJOR
+// set for a head-major pool.  False for an unknown element type or flag.
+inline bool split_format(int32_t format, int32_t& dtype, bool& head_major) {
+  head_major = (format & PA_HEAD_MAJOR) != 0;
+  dtype = format & ~PA_HEAD_MAJOR;
+  return dtype == PA_F32 || dtype == PA_BF16;
+}
+
+// Element strides of a token row and of a kv head within a page (DecodeArgs).
+inline void pool_strides(bool head_major, int page_size, int kv_heads, int head_dim,
+                         int& row_stride, int& head_stride) {
+  row_stride = head_major ? head_dim : kv_heads * head_dim;
+  head_stride = head_major ? page_size * head_dim : head_dim;
+}
 
 // Rows attended by a sequence with `ctx` rows: [lo, L) with L = ctx clamped to
 // [0, max_ctx]; with a window W > 0 the new token and at most W - 1 before it, i.e.

@@ -119,12 +119,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
-  const uint32_t page_bytes = row_bytes * (uint32_t)P;
+  const uint32_t row_bytes = (uint32_t)a.row_stride * 2;
+  const uint32_t page_bytes = (uint32_t)Hkv * HD * 2 * (uint32_t)P;
   const int col = lane & 15;           // K token / score head / V 16-byte column block
   const int grp = lane >> 4;           // K head_dim slice / score token group / V token
-  const uint32_t k_lane = (uint32_t)g * HD * 2 + grp * 64;
-  const uint32_t v_lane = (uint32_t)g * HD * 2 + col * 16;
+  const uint32_t head_off = (uint32_t)g * (uint32_t)a.head_stride * 2;
+  const uint32_t k_lane = head_off + grp * 64;
+  const uint32_t v_lane = head_off + col * 16;
   const int last_page = a.num_pages - 1;
 
   // query vectors of the group as the B operand: head col, head_dim slice grp

@@ -480,8 +480,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const int last_page = a.num_pages - 1;
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
-  const uint32_t page_bytes = row_bytes * (uint32_t)P;
+  const uint32_t row_bytes = (uint32_t)a.row_stride * 2;      // one token's row of a head
+  const uint32_t head_bytes = (uint32_t)a.head_stride * 2;    // one kv head within a page
+  const uint32_t page_bytes = (uint32_t)Hkv * HD * 2 * (uint32_t)P;
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       const uint32_t bits = ((1u << hi_off) - 1u) & (~((1u << lo_off) - 1u) | ((1u << sl_off) - 1u));
       Tl.valid = mapped ? bits : 0u;
       const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
-                            (uint32_t)(ut0 & (P - 1)) * row_bytes + (uint32_t)ug * HD * 2;
+                            (uint32_t)(ut0 & (P - 1)) * row_bytes + (uint32_t)ug * head_bytes;
       const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     const int tk = t0 + col;
     Tl.valid = (uint32_t)(__ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e >= 0 &&
                                    e <= last_page) & 0xffffull);
-    const uint32_t hoff = (uint32_t)d.g * HD * 2;
+    const uint32_t hoff = (uint32_t)d.g * head_bytes;
     const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
     const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 16);
 #pragma unroll

@@ -33,22 +33,28 @@ namespace pa {
 
 // ------------------------------------------------------------------------------------
 // store_kv: one block per new token (grid-stride over tokens).  Rows move in units of U
-// (16 bytes when every pointer and the row size allow it, else 4 bytes).
+// (16 bytes when every pointer and the row size allow it, else 4 bytes).  A new row is
+// kv_heads pieces of units_per_head units; in the pool, slot page * P + r puts piece h at
+// unit page * P * units_per_row + r * row_units + h * head_units (token-major pools pass
+// the whole row as one piece).
 // ------------------------------------------------------------------------------------
 template <typename U>
 __global__ __launch_bounds__(256) void store_kv_kernel(
     U* __restrict__ kp, U* __restrict__ vp, const U* __restrict__ kn, const U* __restrict__ vn,
-    const int32_t* __restrict__ slots, int num_tokens, int64_t num_slots, int units_per_row) {
+    const int32_t* __restrict__ slots, int num_tokens, int64_t num_slots, int units_per_row,
+    int page_size, int units_per_head, int row_units, int head_units) {
   for (int t = blockIdx.x; t < num_tokens; t += gridDim.x) {
     const int slot = slots[t];
     if (slot < 0 || (int64_t)slot >= num_slots) continue;
     const U* ks = kn + (size_t)t * units_per_row;
     const U* vs = vn + (size_t)t * units_per_row;
-    U* kd = kp + (size_t)slot * units_per_row;
-    U* vd = vp + (size_t)slot * units_per_row;
+    const size_t base = (size_t)(slot / page_size) * page_size * units_per_row +
+                        (size_t)(slot % page_size) * row_units;
     for (int i = threadIdx.x; i < units_per_row; i += blockDim.x) {
-      kd[i] = ks[i];
-      vd[i] = vs[i];
+      const int h = i / units_per_head;
+      const size_t o = base + (size_t)h * head_units + (i - h * units_per_head);
+      kp[o] = ks[i];
+      vp[o] = vs[i];
     }
   }
 }
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
   const T* kp = reinterpret_cast<const T*>(a.k_pool);
   const T* vp = reinterpret_cast<const T*>(a.v_pool);
-  const size_t row_stride = (size_t)Hkv * D;
+  const size_t page_elems = (size_t)a.page_size * Hkv * D;
   const int32_t* btr = a.block_tables + (size_t)(a.row_seq ? a.row_seq[s] : s) * a.bt_stride;
   int t_begin, t_end;
   chunk_span(c, L, sl, lo, a.chunk, t_begin, t_end);
@@ -171,8 +177,8 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
       const int page = btr[t / a.page_size];
       valid = page >= 0 && page < a.num_pages;
       if (valid) {
-        const size_t off = ((size_t)page * a.page_size + t % a.page_size) * row_stride +
-                           (size_t)g * D + sub * EPL;
+        const size_t off = (size_t)page * page_elems + (size_t)(t % a.page_size) * a.row_stride +
+                           (size_t)g * a.head_stride + sub * EPL;
         load16<T>(kp + off, kx);
         load16<T>(vp + off, vx);
       }
@@ -404,24 +410,33 @@ extern "C" int pa_store_kv(void* k_pool, void* v_pool, const void* k_new, const 
                            void* stream) {
   if (num_tokens < 0 || num_pages <= 0 || page_size <= 0 || kv_heads <= 0 || head_dim <= 0)
     return PA_EINVAL;
-  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  bool head_major;
+  if (!split_format(dtype, dtype, head_major)) return PA_EINVAL;
   if (num_tokens == 0) return PA_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_EINVAL;
-  const int64_t row_bytes = (int64_t)kv_heads * head_dim * elt_bytes(dtype);
-  if (row_bytes % 4) return PA_EUNSUPPORTED;
+  const int64_t head_bytes = (int64_t)head_dim * elt_bytes(dtype);
+  const int64_t row_bytes = head_bytes * kv_heads;
+  // a head-major pool moves a row head by head: each piece must be whole units
+  const int64_t piece = head_major ? head_bytes : row_bytes;
+  if (piece % 4) return PA_EUNSUPPORTED;
   const int64_t num_slots = (int64_t)num_pages * page_size;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int grid = num_tokens < 65535 ? num_tokens : 65535;
-  if (row_bytes % 16 == 0 && aligned16(k_pool) && aligned16(v_pool) && aligned16(k_new) &&
+  int rs, hs;
+  pool_strides(head_major, page_size, kv_heads, head_dim, rs, hs);
+  const int eb = elt_bytes(dtype);
+  if (piece % 16 == 0 && aligned16(k_pool) && aligned16(v_pool) && aligned16(k_new) &&
       aligned16(v_new)) {
     hipLaunchKernelGGL(store_kv_kernel<uint4>, dim3(grid), dim3(128), 0, st,
                        (uint4*)k_pool, (uint4*)v_pool, (const uint4*)k_new, (const uint4*)v_new,
-                       slot_mapping, num_tokens, num_slots, (int)(row_bytes / 16));
+                       slot_mapping, num_tokens, num_slots, (int)(row_bytes / 16), page_size,
+                       (int)(piece / 16), rs * eb / 16, hs * eb / 16);
   } else {
     hipLaunchKernelGGL(store_kv_kernel<uint32_t>, dim3(grid), dim3(128), 0, st,
                        (uint32_t*)k_pool, (uint32_t*)v_pool, (const uint32_t*)k_new,
                        (const uint32_t*)v_new, slot_mapping, num_tokens, num_slots,
-                       (int)(row_bytes / 4));
+                       (int)(row_bytes / 4), page_size, (int)(piece / 4), rs * eb / 4,
+                       hs * eb / 4);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
@@ -432,7 +447,8 @@ extern "C" int pa_copy_pages(void* k_pool, void* v_pool, const int32_t* src_page
                              int32_t dtype, void* stream) {
   if (num_copies < 0 || num_pages <= 0 || page_size <= 0 || kv_heads <= 0 || head_dim <= 0)
     return PA_EINVAL;
-  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  bool head_major;   // a page holds the same bytes in either layout: copied whole
+  if (!split_format(dtype, dtype, head_major)) return PA_EINVAL;
   if (num_copies == 0) return PA_OK;
   if (!k_pool || !v_pool || !src_pages || !dst_pages) return PA_EINVAL;
   const int64_t page_bytes = (int64_t)page_size * kv_heads * head_dim * elt_bytes(dtype);
@@ -469,7 +485,8 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
       page_size <= 0 || bt_stride <= 0)
     return PA_EINVAL;
   if (q_heads % kv_heads) return PA_EINVAL;
-  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  bool head_major;
+  if (!split_format(dtype, dtype, head_major)) return PA_EINVAL;
   if (!(scale == scale)) return PA_EINVAL;
   const int group = q_heads / kv_heads;
   const int64_t table_rows = (int64_t)bt_stride * page_size;
@@ -487,6 +504,7 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
   DecodeArgs a{};
   a.hints = hints;
   a.sinks = window > 0 ? sinks : 0;
+  pool_strides(head_major, page_size, kv_heads, head_dim, a.row_stride, a.head_stride);
   if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
                        max_live, run_sinks)) {
     // balanced streaming path: wavefronts and chunks sized to the largest possible list
@@ -630,7 +648,8 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
     return PA_EINVAL;
   if (num_q > 0 && (num_seqs == 0 || max_q_len <= 0)) return PA_EINVAL;
   if (q_heads % kv_heads) return PA_EINVAL;
-  if (dtype != PA_F32 && dtype != PA_BF16) return PA_EINVAL;
+  bool head_major;
+  if (!split_format(dtype, dtype, head_major)) return PA_EINVAL;
   if (!(scale == scale)) return PA_EINVAL;
   const int group = q_heads / kv_heads;
   const int64_t table_rows = (int64_t)bt_stride * page_size;
@@ -648,6 +667,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
   const int max_live = window > 0 && window < max_context_len ? window : max_context_len;
 
   DecodeArgs a{};
+  pool_strides(head_major, page_size, kv_heads, head_dim, a.row_stride, a.head_stride);
   a.out = out;
   a.q = q;
   a.k_pool = k_pool;

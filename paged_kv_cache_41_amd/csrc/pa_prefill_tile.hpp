@@ -218,10 +218,10 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
 
   const int P = a.page_size;
   const int lp = 31 - __clz(P);
-  const uint32_t row_bytes = (uint32_t)Hkv * HD * 2;
-  const uint32_t page_bytes = row_bytes * (uint32_t)P;
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * HD * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * HD * 2;
+  const uint32_t row_bytes = (uint32_t)a.row_stride * 2;
+  const uint32_t page_bytes = (uint32_t)Hkv * HD * 2 * (uint32_t)P;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * a.head_stride * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * a.head_stride * 2;
   const int32_t* btr = a.block_tables + (size_t)s * a.bt_stride;
   const int last_page = a.num_pages - 1;
 

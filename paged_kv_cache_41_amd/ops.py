@@ -45,16 +45,31 @@ def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> int:
     return s.cuda_stream
 
 
-def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor):
+LAYOUTS = ("token", "head")
+
+
+def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor, layout: str = "token"):
+    """(num_pages, page_size, kv_heads, head_dim) of the pools.  ``layout="token"``:
+    ``[num_pages, page_size, kv_heads, head_dim]``; ``"head"`` (head-major):
+    ``[num_pages, kv_heads, page_size, head_dim]``."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {LAYOUTS}")
     if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.dtype != v_pool.dtype:
-        raise ValueError("pools must both be [num_pages, page_size, kv_heads, head_dim]")
-    return tuple(int(x) for x in k_pool.shape)
+        raise ValueError("pools must both be 4-D, of one shape and dtype")
+    n, a, b, d = (int(x) for x in k_pool.shape)
+    return (n, a, b, d) if layout == "token" else (n, b, a, d)
 
 
-def store_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
+def _fmt(t: torch.Tensor, layout: str) -> int:
+    """The dtype argument of a call on pools of this layout."""
+    return _code(t) | (_lib.PA_HEAD_MAJOR if layout == "head" else 0)
+
+
+def store_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None,
+             layout: str = "token") -> None:
     """Write row t of k_new/v_new to flat slot slot_mapping[t] of the pools (in place)."""
     dev = _dev(k_pool, v_pool, k_new, v_new, slot_mapping)
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     T = int(slot_mapping.numel())
     if k_new.shape != (T, hkv, d) or v_new.shape != (T, hkv, d):
         raise ValueError("new rows must be [num_tokens, kv_heads, head_dim]")
@@ -64,13 +79,14 @@ def store_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
     lib = _lib.load()
     _lib.check("pa_store_kv", lib.pa_store_kv(
         k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-        slot_mapping.data_ptr(), T, n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
+        slot_mapping.data_ptr(), T, n, P, hkv, d, _fmt(k_pool, layout), _stream(dev, stream)))
 
 
-def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
+def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None,
+               layout: str = "token") -> None:
     """pool[dst[i]] = pool[src[i]] for K and V, whole pages (in place)."""
     dev = _dev(k_pool, v_pool, src_pages, dst_pages)
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     if src_pages.numel() != dst_pages.numel():
         raise ValueError("source and target lists differ in length")
     _i32(src_pages, "src_pages")
@@ -78,7 +94,7 @@ def copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
     lib = _lib.load()
     _lib.check("pa_copy_pages", lib.pa_copy_pages(
         k_pool.data_ptr(), v_pool.data_ptr(), src_pages.data_ptr(), dst_pages.data_ptr(),
-        int(src_pages.numel()), n, P, hkv, d, _code(k_pool), _stream(dev, stream)))
+        int(src_pages.numel()), n, P, hkv, d, _fmt(k_pool, layout), _stream(dev, stream)))
 
 
 def reset_workspace(workspace: torch.Tensor, stream=None) -> None:
@@ -93,15 +109,15 @@ def reset_workspace(workspace: torch.Tensor, stream=None) -> None:
 
 
 def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
-                 max_context_len, ws_ptr, ws_size, stream_handle, hints=0):
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+                 max_context_len, ws_ptr, ws_size, stream_handle, hints=0, layout="token"):
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     B, hq, dq = (int(x) for x in q.shape)
     lib = _lib.load()
     size = ctypes.c_size_t(ws_size)
     head = (out.data_ptr() if out is not None else None, q.data_ptr(), k_pool.data_ptr(),
             v_pool.data_ptr(), block_tables.data_ptr(), int(block_tables.shape[1]),
             context_lens.data_ptr(), B, hq, hkv, d, n, P, int(window))
-    tail = (int(max_context_len), float(scale), _code(q), ws_ptr, ctypes.byref(size),
+    tail = (int(max_context_len), float(scale), _fmt(q, layout), ws_ptr, ctypes.byref(size),
             stream_handle)
     if hints:
         _lib.check("pa_decode_hinted",
@@ -114,17 +130,21 @@ def _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sin
 
 
 def decode_workspace_bytes(q, k_pool, v_pool, block_tables, context_lens, *, window=0,
-                           sinks=0, max_context_len=0) -> int:
+                           sinks=0, max_context_len=0, layout: str = "token") -> int:
     """Bytes of device workspace ``decode`` needs for these operands."""
     return _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, sinks,
-                        1.0, max_context_len, None, 0, None)
+                        1.0, max_context_len, None, 0, None, layout=layout)
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
            sinks: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           stream=None, unshared_pages: bool = False) -> torch.Tensor:
+           stream=None, unshared_pages: bool = False, layout: str = "token") -> torch.Tensor:
     """Single-query paged attention; returns fp32 ``[num_seqs, q_heads, head_dim]``.
+
+    ``layout="head"`` takes head-major pools ``[num_pages, kv_heads, page_size,
+    head_dim]`` (``PA_HEAD_MAJOR``); the result is bit-identical to the same call on
+    token-major pools holding the same rows.
 
     A raw token-slot table is passed as ``block_tables`` together with pools
     viewed in pages of one row (``pool.view(-1, 1, kv_heads, head_dim)``).
@@ -139,7 +159,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     allocated for this call.
     """
     dev = _dev(q, k_pool, v_pool, block_tables, context_lens)
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
         raise ValueError("q must be [num_seqs, q_heads, head_dim] in the pool dtype")
     B = int(q.shape[0])
@@ -154,7 +174,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     elif out.shape != (B, q.shape[1], d) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 [num_seqs, q_heads, head_dim]")
     need = _decode_call(None, q, k_pool, v_pool, block_tables, context_lens, window, sinks,
-                        scale, max_context_len, None, 0, None)
+                        scale, max_context_len, None, 0, None, layout=layout)
     # (an empty tensor's pointer is NULL, which the library reads as a size query: even
     # when the call needs no workspace it gets a byte of its own)
     if workspace is None or workspace.numel() == 0 or \
@@ -163,18 +183,19 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, window: int = 0,
     _decode_call(out, q, k_pool, v_pool, block_tables, context_lens, window, sinks, scale,
                  max_context_len, workspace.data_ptr(),
                  workspace.numel() * workspace.element_size(), _stream(dev, stream),
-                 _lib.PA_HINT_UNSHARED if unshared_pages else 0)
+                 _lib.PA_HINT_UNSHARED if unshared_pages else 0, layout=layout)
     return out
 
 
 def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, *, out: torch.Tensor,
                    window: int = 0, sinks: int = 0, scale: Optional[float] = None,
-                   max_context_len: int = 0, stream=None, unshared_pages: bool = False) -> torch.Tensor:
+                   max_context_len: int = 0, stream=None, unshared_pages: bool = False,
+                   layout: str = "token") -> torch.Tensor:
     """``decode`` through ``pa_decode_noalloc``: no workspace, nothing allocated (the
     caller passes ``out``).  The library's one scratch buffer per GPU serves every such
     call, so calls that overlap on one GPU race."""
     dev = _dev(q, k_pool, v_pool, block_tables, context_lens, out)
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     B, hq = int(q.shape[0]), int(q.shape[1])
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
         raise ValueError("q must be [num_seqs, q_heads, head_dim] in the pool dtype")
@@ -191,13 +212,14 @@ def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, *, out: torch.
         out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), B, hq, hkv,
         d, n, P, int(window), int(sinks), _lib.PA_HINT_UNSHARED if unshared_pages else 0,
-        int(max_context_len), float(scale), _code(q), _stream(dev, stream)))
+        int(max_context_len), float(scale), _fmt(q, layout), _stream(dev, stream)))
     return out
 
 
 def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
-                  window, scale, max_context_len, ws_ptr, ws_size, stream_handle):
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+                  window, scale, max_context_len, ws_ptr, ws_size, stream_handle,
+                  layout="token"):
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     num_q, hq, _ = (int(x) for x in q.shape)
     B = int(context_lens.shape[0])
     lib = _lib.load()
@@ -206,26 +228,27 @@ def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, m
         out.data_ptr() if out is not None else None, q.data_ptr(), q_start.data_ptr(),
         k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
         int(block_tables.shape[1]), context_lens.data_ptr(), B, num_q, int(max_q_len), hq, hkv,
-        d, n, P, int(window), int(max_context_len), float(scale), _code(q), ws_ptr,
+        d, n, P, int(window), int(max_context_len), float(scale), _fmt(q, layout), ws_ptr,
         ctypes.byref(size), stream_handle))
     return size.value
 
 
 def prefill_workspace_bytes(q, q_start, k_pool, v_pool, block_tables, context_lens, *,
                             max_q_len: int, window: int = 0, scale: Optional[float] = None,
-                            max_context_len: int = 0) -> int:
+                            max_context_len: int = 0, layout: str = "token") -> int:
     """Bytes of device workspace ``prefill`` needs for these operands (and scale: the
     kernel that serves long chunks needs none, and takes positive scales only)."""
     if scale is None:
         scale = int(q.shape[-1]) ** -0.5
     return _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens,
-                         max_q_len, window, scale, max_context_len, None, 0, None)
+                         max_q_len, window, scale, max_context_len, None, 0, None,
+                         layout=layout)
 
 
 def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len: int,
             window: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            stream=None) -> torch.Tensor:
+            stream=None, layout: str = "token") -> torch.Tensor:
     """Several query tokens per sequence (``pa_prefill``); returns fp32 ``[num_q, q_heads, head_dim]``.
 
     ``q`` is ``[num_q, q_heads, head_dim]``; the query rows of sequence ``s`` are
@@ -234,7 +257,7 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
     ``decode``.
     """
     dev = _dev(q, q_start, k_pool, v_pool, block_tables, context_lens)
-    n, P, hkv, d = _pool_dims(k_pool, v_pool)
+    n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
         raise ValueError("q must be [num_q, q_heads, head_dim] in the pool dtype")
     B = int(context_lens.shape[0])
@@ -253,7 +276,7 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
     elif out.shape != (num_q, q.shape[1], d) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 [num_q, q_heads, head_dim]")
     need = _prefill_call(None, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
-                         window, scale, max_context_len, None, 0, None)
+                         window, scale, max_context_len, None, 0, None, layout=layout)
     # (an empty tensor's pointer is NULL, which the library reads as a size query: even
     # when the call needs no workspace it gets a byte of its own)
     if workspace is None or workspace.numel() == 0 or \
@@ -261,7 +284,8 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, window,
                   scale, max_context_len, workspace.data_ptr(),
-                  workspace.numel() * workspace.element_size(), _stream(dev, stream))
+                  workspace.numel() * workspace.element_size(), _stream(dev, stream),
+                  layout=layout)
     return out
 
 

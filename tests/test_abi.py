@@ -126,3 +126,47 @@ def test_every_workspace_size_includes_the_counter_header():
         assert lib.pa_decode(None, None, None, None, None, 256, None, 3, 8, 2, d, 100, 16, 0,
                              64, 1.0, dtype, None, ctypes.byref(size), None) == _lib.PA_OK
         assert size.value > _lib.PA_WORKSPACE_HEADER, (dtype, d)
+
+
+def test_head_major_flag_validation_needs_no_gpu():
+    """PA_HEAD_MAJOR is accepted by every call that takes the pools; any other bit in the
+    dtype argument is rejected; the workspace a decode or prefill needs does not depend
+    on the layout."""
+    lib = _lib.load()
+    HM = _lib.PA_HEAD_MAJOR
+    size = ctypes.c_size_t(0)
+
+    def dec(dt, d=128):
+        size.value = 0
+        rc = lib.pa_decode(None, None, None, None, None, 256, None, 64, 32, 8, d, 1000, 16, 0,
+                           4096, 1.0, dt, None, ctypes.byref(size), None)
+        return rc, size.value
+
+    def pre(dt):
+        size.value = 0
+        rc = lib.pa_prefill(None, None, None, None, None, None, 256, None, 4, 32, 8, 32, 8, 128,
+                            1000, 16, 0, 4096, 1.0, dt, None, ctypes.byref(size), None)
+        return rc, size.value
+
+    for dt in (_lib.PA_BF16, _lib.PA_F32):
+        assert dec(dt | HM) == dec(dt) and dec(dt)[0] == _lib.PA_OK
+        assert dec(dt | HM, 64) == dec(dt, 64)
+        assert pre(dt | HM) == pre(dt) and pre(dt)[0] == _lib.PA_OK
+        assert dec(dt | 0x200)[0] == _lib.PA_EINVAL
+        assert pre(dt | 0x200)[0] == _lib.PA_EINVAL
+        assert lib.pa_store_kv(None, None, None, None, None, 0, 8, 16, 8, 128, dt | HM,
+                               None) == _lib.PA_OK
+        assert lib.pa_store_kv(None, None, None, None, None, 0, 8, 16, 8, 128, dt | 0x200,
+                               None) == _lib.PA_EINVAL
+        assert lib.pa_copy_pages(None, None, None, None, 0, 8, 16, 8, 128, dt | HM,
+                                 None) == _lib.PA_OK
+        assert lib.pa_copy_pages(None, None, None, None, 0, 8, 16, 8, 128, dt | 0x200,
+                                 None) == _lib.PA_EINVAL
+    hinted = lib.pa_decode_hinted(None, None, None, None, None, 256, None, 64, 32, 8, 128, 1000,
+                                  16, 1024, 4, _lib.PA_HINT_UNSHARED, 4096, 1.0,
+                                  _lib.PA_BF16 | HM, None, ctypes.byref(size), None)
+    assert hinted == _lib.PA_OK and size.value > 0
+    # a head-major bf16 row of head_dim 1 is 2 bytes: no 4-byte units to move
+    fake = ctypes.c_void_p(256)
+    assert lib.pa_store_kv(fake, fake, fake, fake, fake, 1, 8, 16, 8, 1, _lib.PA_BF16 | HM,
+                           None) == _lib.PA_EUNSUPPORTED

@@ -1,0 +1,139 @@
+"""Head-major pools (PA_HEAD_MAJOR, pools [num_pages, kv_heads, page_size, head_dim]).
+
+Each case runs copy -> store -> attention twice from the same rows: on token-major
+pools and on the same pools transposed to head-major.  Only where a row sits in its page
+differs, so the pools after the step (transposed back) and the outputs must agree bit
+for bit; where the oracle is cheap the head-major output is also checked against it.
+Every decode and prefill path is covered: the streaming kernel (tiles in one page, the
+cache-hinted variant, pages under 16 rows, the aligned window partition, sinks, several
+query tokens), the per-row kernels (fp32, head_dim 64), the chunked path above the
+streaming limit, the prefill tile kernel, and copy-on-write copies.  Raw slot tables
+address pools viewed as pages of one row, which only the token-major layout allows, so
+they are not a case here.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import bits, expected_step
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_41_amd import _lib
+    _lib.load()
+
+
+def ops():
+    from paged_kv_cache_41_amd import ops as _ops
+    return _ops
+
+
+_GQA = dict(dtype="bf16", q_heads=32, kv_heads=8, head_dim=128)
+
+# name -> (scenario builder, cache hint, sequences the oracle checks: "all", a count, or 0)
+CASES = {
+    "gqa_b64": (lambda: workloads.make_config(2, device="cuda"), False, "all"),
+    "gqa_b64_unshared": (lambda: workloads.make_config(2, device="cuda"), True, "all"),
+    "window_b32_aligned": (lambda: workloads.make_config(3, device="cuda"), True, "all"),
+    "sinks_w64_s5": (lambda: workloads.build(workloads.Spec(
+        name="hm_sinks", num_seqs=24, page_size=16, window=64, sinks=5, len_lo=1, len_hi=300,
+        spare="nan", **_GQA), 61, device="cuda"), False, "all"),
+    "page4": (lambda: workloads.build(workloads.Spec(
+        name="hm_p4", num_seqs=16, page_size=4, len_lo=1, len_hi=500, spare="nan", **_GQA),
+        62, device="cuda"), False, "all"),
+    "page64": (lambda: workloads.build(workloads.Spec(
+        name="hm_p64", num_seqs=16, page_size=64, len_lo=1, len_hi=2000, spare="nan", **_GQA),
+        63, device="cuda"), False, "all"),
+    "f32_rows": (lambda: workloads.build(workloads.Spec(
+        name="hm_f32", dtype="f32", num_seqs=6, q_heads=8, kv_heads=2, head_dim=64,
+        page_size=16, len_lo=1, len_hi=200, spare="nan"), 64, device="cuda"), False, "all"),
+    "bf16_d64_rows": (lambda: workloads.build(workloads.Spec(
+        name="hm_d64", dtype="bf16", num_seqs=6, q_heads=8, kv_heads=2, head_dim=64,
+        page_size=8, len_lo=1, len_hi=200, spare="nan"), 65, device="cuda"), False, "all"),
+    "b2100_chunked": (lambda: workloads.build(workloads.Spec(
+        name="hm_b2100", dtype="bf16", num_seqs=2100, q_heads=16, kv_heads=4, head_dim=128,
+        page_size=16, window=40, len_lo=1, len_hi=300), 66, device="cuda"), False, 40),
+    "prefix_cow": (lambda: workloads.make_config(4, device="cuda"), False, 24),
+    "verify_q4": (lambda: workloads.make_config(2, device="cuda", q_lo=4, q_hi=4,
+                                                name="gqa_b64_q4"), False, 0),
+    "prefill_q128_tile": (lambda: workloads.make_config(2, device="cuda", q_lo=128, q_hi=128,
+                                                        name="gqa_b64_q128"), False, 0),
+    "prefill_f32_rows": (lambda: workloads.build(workloads.Spec(
+        name="hm_pre_f32", dtype="f32", num_seqs=5, q_heads=8, kv_heads=2, head_dim=64,
+        page_size=16, len_lo=1, len_hi=100, q_lo=1, q_hi=6, spare="nan"), 67, device="cuda"),
+        False, "all"),
+}
+
+
+def _step(sc, kp, vp, layout, unshared):
+    o = ops()
+    s = sc.spec
+    o.copy_pages(kp, vp, sc.copy_src, sc.copy_dst, layout=layout)
+    o.store_kv(kp, vp, sc.k_new, sc.v_new, sc.slot_mapping, layout=layout)
+    if sc.q_start is not None:
+        out = o.prefill(sc.q, sc.q_start, kp, vp, sc.block_tables, sc.context_lens,
+                        max_q_len=max(int(sc.nq.max()), 1), window=s.window, scale=sc.scale,
+                        max_context_len=sc.max_context_len, layout=layout)
+    else:
+        out = o.decode(sc.q, kp, vp, sc.block_tables, sc.context_lens, window=s.window,
+                       sinks=s.sinks, scale=sc.scale, max_context_len=sc.max_context_len,
+                       unshared_pages=unshared, layout=layout)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_head_major_matches_token_major(case):
+    build, unshared, check = CASES[case]
+    sc = build()
+    print(f"case {case} seed {sc.seed}", flush=True)
+    assert sc.table_page_size == sc.spec.page_size
+    kp0, vp0 = bits(sc.k_pool), bits(sc.v_pool)
+    hk = sc.k_pool.transpose(1, 2).contiguous()
+    hv = sc.v_pool.transpose(1, 2).contiguous()
+    out_t = _step(sc, sc.k_pool, sc.v_pool, "token", unshared)
+    out_h = _step(sc, hk, hv, "head", unshared)
+    assert np.array_equal(bits(hk.transpose(1, 2)), bits(sc.k_pool)), "K pools differ"
+    assert np.array_equal(bits(hv.transpose(1, 2)), bits(sc.v_pool)), "V pools differ"
+    assert np.array_equal(bits(out_h), bits(out_t)), "outputs differ"
+    if not check:
+        return
+    B = sc.spec.num_seqs
+    seqs = None
+    if check != "all":
+        rng = np.random.default_rng(5)
+        seqs = sorted(set(rng.choice(B, check, replace=False).tolist()) |
+                      {0, B - 1, int(np.argmax(sc.lens))})
+    kp, vp, ref = expected_step(sc, seqs=seqs, k_pool_bits=kp0, v_pool_bits=vp0)
+    assert np.array_equal(bits(sc.k_pool), kp) and np.array_equal(bits(sc.v_pool), vp)
+    got = out_h.cpu().double().numpy()
+    got = got if seqs is None else got[seqs]
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= TOL[sc.spec.dtype], f"{case}: max abs error {err:.3g}"
+
+
+def test_head_major_page_size_one_is_the_same_bytes():
+    """With pages of one row the two layouts are the same bytes: a head-major call on the
+    token-major pools themselves gives the token-major result."""
+    spec = workloads.Spec(name="hm_p1", num_seqs=8, page_size=1, len_lo=1, len_hi=300,
+                          spare="nan", **_GQA)
+    sc = workloads.build(spec, 68, device="cuda")
+    print(f"case page1 seed {sc.seed}", flush=True)
+    n, _, hkv, d = sc.k_pool.shape
+    # the same bytes in the head-major shape [num_pages, kv_heads, 1, head_dim]
+    kp = sc.k_pool.clone().view(n, hkv, 1, d)
+    vp = sc.v_pool.clone().view(n, hkv, 1, d)
+    out_t = _step(sc, sc.k_pool, sc.v_pool, "token", False)
+    out_h = _step(sc, kp, vp, "head", False)
+    assert np.array_equal(bits(kp).ravel(), bits(sc.k_pool).ravel())
+    assert np.array_equal(bits(vp).ravel(), bits(sc.v_pool).ravel())
+    assert np.array_equal(bits(out_h), bits(out_t))
