@@ -446,7 +446,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // ---- the partition and this wavefront's range ----------------------------------------
   const int T = uni(Hkv * st_cum[B]);
   Part part_of{false, T, min(a.total_waves, T)};
-  if constexpr (!MULTI && ALIGN) {
+  if constexpr (ALIGN) {
     // Aligned partition: workgroup g takes segments g NSEG / NWG to (g + 1) NSEG / NWG - 1
     // (NSEG = B Hkv, split by count: even segments give even workgroups, with no drift);
     // it is used when no workgroup then holds more than 1/16 above the mean.  Every
@@ -695,8 +695,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
             o[1] = make_float4(ac[4][r] * inv, ac[5][r] * inv, ac[6][r] * inv, ac[7][r] * inv);
           }
         }
-      } else if (!MULTI && part_of.aligned) {
+      } else if (part_of.aligned) {
         // aligned partition: the piece's partial stays in LDS for the workgroup's combine
+        // (one block of 16 columns: with ALIGN, NB is at most 1)
         float* pl = st_part[w][first_seg ? 0 : 1];
         if (lane < C) {
           pl[2 * lane] = m_ref[i];
@@ -922,7 +923,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
-          if (!MULTI && part_of.aligned) {
+          if (part_of.aligned) {
             // the piece of wavefront k - NW blockIdx of this workgroup, from LDS
             const float* pl = st_part[k - (int)blockIdx.x * NW][k == k1 ? slot1 : 0];
             ml[b] = make_float2(pl[2 * h], pl[2 * h + 1]);
@@ -962,7 +963,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       for (int q = 0; q < QPL; ++q)
         o[q] = make_float4(nm[q].x * inv, nm[q].y * inv, nm[q].z * inv, nm[q].w * inv);
     }
-    if (sl == 0 && !(!MULTI && part_of.aligned))
+    if (sl == 0 && !part_of.aligned)
       __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   // ---- cut segments: the piece that arrives last combines them ---------------------------
@@ -974,29 +975,26 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // after this wavefront's partial stores have completed (vmcnt reaches 0), so a
   // wavefront that sees the full count reads complete partials.  No cache-wide write-back
   // or invalidate is needed: nothing is exchanged through ordinary cached stores.
-  if constexpr (!MULTI) {
-    if (part_of.aligned) {
-      // every piece of a cut segment lies in this workgroup: after the barrier the wavefront
-      // holding a segment's first piece combines it from LDS.  A workgroup with fewer tiles
-      // than wavefronts has empty ranges, which can lie between a segment's first and last
-      // pieces: they publish a running max of -inf, a piece the combine skips.
-      if (n == 0 && lane < C) {
-        st_part[w][0][2 * lane] = -INFINITY;
-        st_part[w][1][2 * lane] = -INFINITY;
-      }
-      __syncthreads();
-      const bool own0 = cut0 && k1_0 == kw, own1 = cut1 && k1_1 == kw;
-      if (own0 && own1) {
-        const bool hi = lane >= 32;
-        combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0,
-                hi ? k1_1 : k1_0, hi ? k2_1 : k2_0);
-      } else if (own0) {
-        combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
-      } else if (own1) {
-        combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
-      }
-      return;
+  if (part_of.aligned) {
+    // every piece of a cut segment lies in this workgroup: after the barrier the wavefront
+    // holding a segment's first piece combines it from LDS.  A workgroup with fewer tiles
+    // than wavefronts has empty ranges, which can lie between a segment's first and last
+    // pieces: they publish a running max of -inf, a piece the combine skips.
+    if (n == 0 && lane < C) {
+      st_part[w][0][2 * lane] = -INFINITY;
+      st_part[w][1][2 * lane] = -INFINITY;
     }
+    __syncthreads();
+    const bool own0 = cut0 && k1_0 == kw, own1 = cut1 && k1_1 == kw;
+    if (!MULTI && own0 && own1) {
+      const bool hi = lane >= 32;
+      combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0,
+              hi ? k1_1 : k1_0, hi ? k2_1 : k2_0);
+    } else {
+      if (own0) combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
+      if (own1) combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
+    }
+    return;
   }
   if (!cut0 && !cut1) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1098,11 +1096,11 @@ inline void launch_variant(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 
 }
 
 // Only a kernel built with ALIGN tries the aligned partition, so the others carry none of
-// its branches.
+// its branches.  (Its LDS partials hold one block of 16 columns: NB at most 1.)
 template <int NB>
 inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
-  if (NB == 0 && a.try_aligned)
-    launch_variant<NB, NB == 0>(a, st, grid, block);
+  if (NB <= 1 && a.try_aligned)
+    launch_variant<NB, NB <= 1>(a, st, grid, block);
   else
     launch_variant<NB, false>(a, st, grid, block);
 }

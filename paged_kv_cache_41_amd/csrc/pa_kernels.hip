@@ -715,6 +715,16 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
     if (waves > stream_waves_max) waves = stream_waves_max;
     if (waves < stream::NW) waves = stream::NW;
     waves = (waves + stream::NW - 1) / stream::NW * stream::NW;
+    // groups of one block with a window: whole segments per workgroup when they are even
+    // (as for decode; the bound on the group count sizes the grid, and a batch with fewer
+    // groups keeps the flat split)
+    const int64_t segs = stream::blocks_bound(num_seqs, group, max_q, nb) * kv_heads;
+    if (nb == 1 && window > 0 && window < max_context_len && segs >= 64) {
+      const int64_t wg_max = stream_waves_max / stream::NW;
+      const int64_t k = (segs + wg_max - 1) / wg_max;
+      waves = stream::NW * ((segs + k - 1) / k);
+      a.try_aligned = 1;
+    }
     const size_t need = stream::workspace_bytes((int)waves, 16 * nb);
     if (!workspace) {
       *workspace_bytes = need;

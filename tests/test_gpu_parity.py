@@ -133,7 +133,8 @@ def test_config_slot_table_full():
     check_step(sc)
 
 
-# (sequences, kv heads, window, sinks, context lengths low and high, empty sequences)
+# (sequences, kv heads, window, sinks, context lengths low and high, empty sequences[,
+# query tokens low and high])
 ALIGNED_CASES = {
     # every segment 64 or 65 tiles, one per workgroup
     "one_segment_per_workgroup": (64, 4, 1024, 0, 1024, 3000, 0),
@@ -147,22 +148,28 @@ ALIGNED_CASES = {
     "sinks": (64, 4, 1024, 4, 1100, 3000, 0),
     # contexts mostly inside the window: segments too uneven, the flat split is kept
     "uneven_keeps_flat_split": (64, 4, 1024, 0, 16, 2000, 0),
+    # verify steps (one block of 16 / G = 4 query tokens per sequence): the same split for
+    # segments of query blocks
+    "verify_q4": (64, 4, 1024, 0, 1100, 3000, 0, 4, 4),
+    "verify_q1_to_4": (64, 8, 512, 0, 600, 2000, 0, 1, 4),
+    "verify_uneven_keeps_flat_split": (64, 4, 1024, 0, 16, 2000, 0, 4, 4),
 }
 
 
 @pytest.mark.parametrize("case", sorted(ALIGNED_CASES))
 def test_window_segments_aligned_to_workgroups(case):
     """With a window, the host sizes the grid so that each workgroup can take whole
-    segments; when they are about equal the kernel does so and combines the pieces of a
-    cut segment in LDS, else it keeps the equal flat split.  Either way the result is the
-    oracle's."""
-    B, hkv, window, sinks, lo, hi, empty = ALIGNED_CASES[case]
+    segments (a sequence's kv head, or with several query tokens a block of them); when
+    they are about equal the kernel does so and combines the pieces of a cut segment in
+    LDS, else it keeps the equal flat split.  Either way the result is the oracle's."""
+    B, hkv, window, sinks, lo, hi, empty, *q = ALIGNED_CASES[case]
+    q_lo, q_hi = q if q else (1, 1)
     lens = np.random.default_rng(40 + B + window + sinks + lo).integers(lo, hi, size=B)
     lens[:empty] = 0
     spec = workloads.Spec(name=f"window_aligned_{case}", dtype="bf16", num_seqs=B,
                           q_heads=4 * hkv, kv_heads=hkv, head_dim=128, page_size=16,
                           window=window, sinks=sinks, lens=tuple(int(x) for x in lens),
-                          pool_factor=1.25, spare="nan")
+                          q_lo=q_lo, q_hi=q_hi, pool_factor=1.25, spare="nan")
     sc = workloads.build(spec, 44 + empty, device="cuda")
     # the flat split leaves partials of cut segments past the counter header; the aligned
     # one keeps them in LDS and writes nothing there
@@ -170,7 +177,7 @@ def test_window_segments_aligned_to_workgroups(case):
     ws[4096:] = 0x5A
     _run_on_workspace(sc, ws)
     untouched = bool((ws[4096:] == 0x5A).all())
-    assert untouched == (case != "uneven_keeps_flat_split"), case
+    assert untouched == ("keeps_flat_split" not in case), case
 
 
 @pytest.mark.parametrize("window", [0, 40])
