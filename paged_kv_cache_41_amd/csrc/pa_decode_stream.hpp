@@ -183,6 +183,13 @@ struct Part {
   }
 };
 
+// Table entries of a tile whose rows lie in several pages: lane (col, grp)'s K row and
+// its four V rows.
+struct RowPages {
+  int k;
+  int v[4];
+};
+
 // What the load and compute stages need of one tile.
 enum : int {
   RANGE_FIRST = 1,   // first tile of the range
@@ -503,15 +510,23 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // the attended ones are clamped to one that is, so their entries are mapped pages.
   const __attribute__((address_space(4))) int32_t* bt_const =
       (const __attribute__((address_space(4))) int32_t*)a.block_tables;
+  // Table entries of a tile.  Pages of at least 16 rows: the one page of the tile, read
+  // through the scalar unit.  Smaller pages: each lane reads the page of its K row (token
+  // t0 + col) and those of its four V rows (tokens t0 + 4 grp + j) itself, one tile ahead,
+  // so the V addresses need no lane shuffle while the tile's loads wait to issue.
   auto table_entry = [&](const Desc& d) {
     if constexpr (PAGE_TILES) {
       const int t = d.t0 < d.sl ? d.t0 : min(max(d.t0, d.lo), d.L - 1);
       // num_seqs * bt_stride < 2^31 on this path, so the index fits one scalar register
       return bt_const[uni(d.tr * a.bt_stride + (t >> lp))];
     } else {
-      const int tc = d.t0 + col;
-      const int t = tc < d.sl ? tc : min(max(tc, d.lo), d.L - 1);
-      return a.block_tables[(size_t)d.tr * a.bt_stride + (t >> lp)];
+      const int32_t* row = a.block_tables + (size_t)d.tr * a.bt_stride;
+      auto clamp_row = [&](int tc) { return tc < d.sl ? tc : min(max(tc, d.lo), d.L - 1); };
+      RowPages e;
+      e.k = row[clamp_row(d.t0 + col) >> lp];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e.v[j] = row[clamp_row(d.t0 + 4 * grp + j) >> lp];
+      return e;
     }
   };
 
@@ -527,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const uint32_t k_lane_off = (uint32_t)col * row_bytes + grp * 16;
   const uint32_t v_lane_off = (uint32_t)(4 * grp) * row_bytes + col * 16;
 
-  auto load_tile = [&](const Desc& d, int e, Tile& Tl) {
+  auto load_tile = [&](const Desc& d, const auto& e, Tile& Tl) {
     const int t0 = d.t0;
     if (NB <= 1 && (uni(d.flags) & (RANGE_FIRST | SEG_FIRST))) {
       // the query rows of the group, fetched with the tile so that waiting for them is
@@ -571,22 +586,26 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
       }
-      return;
-    }
+    } else {
     const int tk = t0 + col;
-    Tl.valid = (uint32_t)(__ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e >= 0 &&
-                                   e <= last_page) & 0xffffull);
+    Tl.valid = (uint32_t)(__ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e.k >= 0 &&
+                                   e.k <= last_page) & 0xffffull);
     const uint32_t hoff = (uint32_t)d.g * head_bytes;
     const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
-    const uint4* kp = row_addr(kbase, min(max(e, 0), last_page), tkc, hoff + grp * 16);
+    const uint4* kp = row_addr(kbase, min(max(e.k, 0), last_page), tkc, hoff + grp * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int ev = __shfl(e, 4 * grp + j, 64);
       const int tr = t0 + 4 * grp + j;
       const int tv = tr < d.sl ? tr : min(max(tr, d.lo), d.L - 1);
-      Tl.v[j] = *row_addr(vbase, min(max(ev, 0), last_page), tv, hoff + col * 16);
+      const uint4* vp = row_addr(vbase, min(max(e.v[j], 0), last_page), tv, hoff + col * 16);
+      if constexpr (VNT)
+        Tl.v[j] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vp)));
+      else
+        Tl.v[j] = *vp;
+    }
     }
   };
 
@@ -861,12 +880,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   Desc dsc[DEPTH + 1];
   if (n > 0) {
   Desc d_next = fr.desc();
-  int e_next = table_entry(d_next);
+  auto e_next = table_entry(d_next);
   fr.next();
 #pragma unroll
   for (int u = 0; u < DEPTH; ++u) {
     const Desc d_use = d_next;
-    const int e_use = e_next;
+    const auto e_use = e_next;
     d_next = fr.desc();
     e_next = table_entry(d_next);
     fr.next();
@@ -877,7 +896,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u <= DEPTH; ++u) {
       const Desc d_use = d_next;
-      const int e_use = e_next;
+      const auto e_use = e_next;
       d_next = fr.desc();
       e_next = table_entry(d_next);
       fr.next();
@@ -1085,10 +1104,14 @@ inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
 template <int NB, bool ALIGN>
 inline void launch_variant(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
   constexpr int D = NB > 0 ? STREAM_MULTI_DEPTH : STREAM_DEPTH;
-  if (a.page_size >= TILE && (a.hints & PA_HINT_UNSHARED))
+  const bool unshared = (a.hints & PA_HINT_UNSHARED) != 0;
+  if (a.page_size >= TILE && unshared)
     hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true, ALIGN>), grid, block, 0, st, a);
   else if (a.page_size >= TILE)
     hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, false, ALIGN>), grid, block, 0, st,
+                       a);
+  else if (unshared)
+    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, true, ALIGN>), grid, block, 0, st,
                        a);
   else
     hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, false, ALIGN>), grid, block, 0, st,

@@ -98,19 +98,27 @@ def test_config_window_sinks_full():
     check_step(sc)
 
 
-@pytest.mark.parametrize("cfg,sinks", [(2, 0), (3, 0), (3, 4)])
+@pytest.mark.parametrize("cfg,sinks", [(2, 0), (3, 0), (3, 4), (5, 0), ("page4", 0)])
 def test_unshared_hint_is_bit_identical(cfg, sinks):
     """pa_decode_hinted with PA_HINT_UNSHARED changes only the cache policy of the V
     loads: its output equals the plain call's bit for bit (which the config tests pin to
-    the oracle), on the batch-64 and window workloads, with and without sinks."""
+    the oracle), on the batch-64 and window workloads, with and without sinks, on the raw
+    slot table (pages of one row) and on pages of 4 rows."""
     o = ops()
-    sc = workloads.make_config(cfg, device="cuda", sinks=sinks,
-                               name=f"{workloads.config_spec(cfg).name}_s{sinks}")
+    if cfg == "page4":
+        sc = workloads.build(workloads.Spec(name="hint_p4", num_seqs=32, q_heads=32,
+                                            kv_heads=8, head_dim=128, page_size=4, len_lo=1,
+                                            len_hi=900, spare="nan"), 71, device="cuda")
+    else:
+        sc = workloads.make_config(cfg, device="cuda", sinks=sinks,
+                                   name=f"{workloads.config_spec(cfg).name}_s{sinks}")
     s = sc.spec
+    print(f"case {s.name} seed {sc.seed}", flush=True)
     o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    kv, vv = decode_views(sc)
     outs = []
     for hint in (False, True, True):
-        outs.append(o.decode(sc.q, sc.k_pool, sc.v_pool, sc.block_tables, sc.context_lens,
+        outs.append(o.decode(sc.q, kv, vv, sc.block_tables, sc.context_lens,
                                window=s.window, sinks=s.sinks, scale=sc.scale,
                                max_context_len=sc.max_context_len, unshared_pages=hint))
     torch.cuda.synchronize()
