@@ -547,7 +547,8 @@ def main():
         if multi:
             ops.prefill(sc.q, sc.q_start, kp, vp, sc.block_tables, sc.context_lens,
                         max_q_len=max_q, window=s.window, scale=sc.scale,
-                        max_context_len=sc.max_context_len, out=out, workspace=ws, layout=lay)
+                        max_context_len=sc.max_context_len, out=out, workspace=ws, layout=lay,
+                        unshared_pages=unshared)
         else:
             ops.decode(sc.q, kp, vp, sc.block_tables, sc.context_lens, window=s.window,
                        sinks=s.sinks, scale=sc.scale, max_context_len=sc.max_context_len,
@@ -734,7 +735,8 @@ def main():
                    "launch": ("each step one HIP graph replay (copy, store, attention)"
                               if args.graph else "kernels launched one by one"),
                    "cache_hint": ("unshared pages (the allocator's reference counts): V rows read "
-                                  "with the non-temporal hint" if unshared and not multi else "none")},
+                                  "with the non-temporal hint on the streaming path"
+                                  if unshared else "none")},
         "seqs_per_s": round(s.num_seqs / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * nb["kv"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "step": {"avg_us": round(float(step_ms.mean()) * 1e3, 2),

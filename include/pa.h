@@ -213,8 +213,9 @@ int pa_decode_sinks(float* out, const void* q, const void* k_pool, const void* v
  *                 sequences of the call (no shared prefix, no fork sharing a
  *                 page), so nothing read has a reuse worth caching; the V rows are
  *                 then loaded with the non-temporal cache hint.  Wrong hints
- *                 cost time, not correctness.  Used by the path for bf16 with
- *                 head_dim 128 and page_size >= 16; ignored elsewhere.
+ *                 cost time, not correctness.  Used by the streaming path (bf16,
+ *                 head_dim 128, power-of-two pages, including a raw slot table
+ *                 read as pages of one row); ignored elsewhere.
  *   Errors: PA_EINVAL for other hint bits; otherwise those of pa_decode_sinks.
  */
 #define PA_HINT_UNSHARED 1
@@ -285,6 +286,25 @@ int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_
                int32_t num_pages, int32_t page_size, int32_t window, int32_t max_context_len,
                float scale, int32_t dtype, void* workspace, size_t* workspace_bytes,
                void* stream);
+
+/*
+ * pa_prefill_hinted -- pa_prefill with the hints of pa_decode_hinted, which change
+ * how rows are read, never what is computed: the output is bit-identical to
+ * pa_prefill with the same arguments.
+ *   hints         0 or PA_HINT_UNSHARED (no physical page is attended by two
+ *                 sequences of the call): the V rows are loaded with the
+ *                 non-temporal cache hint on the streaming path (groups of up to
+ *                 two blocks of query tokens); the tile kernel for long chunks,
+ *                 whose query tiles share every K/V block, ignores it.
+ *   Errors: PA_EINVAL for other hint bits; otherwise those of pa_prefill.
+ */
+int pa_prefill_hinted(float* out, const void* q, const int32_t* q_start, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
+                      int32_t max_q_len, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                      int32_t num_pages, int32_t page_size, int32_t window, int32_t hints,
+                      int32_t max_context_len, float scale, int32_t dtype, void* workspace,
+                      size_t* workspace_bytes, void* stream);
 
 /*
  * pa_update_tables -- one step's table changes as one scatter (the mini-sglang

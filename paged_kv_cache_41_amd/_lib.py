@@ -36,6 +36,9 @@ SIGNATURES = {
     "pa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                   _I, _I, _I, ctypes.c_float, _I, _P,
                                   ctypes.POINTER(ctypes.c_size_t), _P]),
+    "pa_prefill_hinted": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I,
+                                         _I, _I, _I, _I, _I, ctypes.c_float, _I, _P,
+                                         ctypes.POINTER(ctypes.c_size_t), _P]),
     "pa_update_tables": (ctypes.c_int, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
     "pa_reset_workspace": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
     "pa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,

@@ -635,14 +635,16 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_pool, const vo
                          max_context_len, scale, dtype, workspace, workspace_bytes, stream);
 }
 
-extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_pool,
-                          const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
-                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
-                          int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
-                          int32_t head_dim, int32_t num_pages, int32_t page_size,
-                          int32_t window, int32_t max_context_len, float scale, int32_t dtype,
-                          void* workspace, size_t* workspace_bytes, void* stream) {
+static int prefill_entry(float* out, const void* q, const int32_t* q_start,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q, int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
+                         int32_t head_dim, int32_t num_pages, int32_t page_size,
+                         int32_t window, int32_t hints, int32_t max_context_len, float scale,
+                         int32_t dtype, void* workspace, size_t* workspace_bytes,
+                         void* stream) {
   if (!workspace_bytes) return PA_EINVAL;
+  if (hints & ~PA_HINT_UNSHARED) return PA_EINVAL;
   if (num_seqs < 0 || num_q < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 ||
       num_pages <= 0 || page_size <= 0 || bt_stride <= 0)
     return PA_EINVAL;
@@ -743,6 +745,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
     a.num_q = num_q;
     a.max_q = max_q;
     a.total_waves = (int)waves;
+    a.hints = hints;
     stream::carve_workspace(a, workspace, 16 * nb);
     return stream::launch(a, st, nb) == 0 ? PA_OK : PA_ELAUNCH;
   }
@@ -777,6 +780,34 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, con
                                      rows_bytes);
   a.ws_acc = a.ws_ml + 2 * parts;
   return launch_rows(a, generic, fast, head_dim, st);
+}
+
+extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_start, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
+                          int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
+                          int32_t head_dim, int32_t num_pages, int32_t page_size,
+                          int32_t window, int32_t max_context_len, float scale, int32_t dtype,
+                          void* workspace, size_t* workspace_bytes, void* stream) {
+  return prefill_entry(out, q, q_start, k_pool, v_pool, block_tables, bt_stride, context_lens,
+                       num_seqs, num_q, max_q_len, q_heads, kv_heads, head_dim, num_pages,
+                       page_size, window, 0, max_context_len, scale, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" int pa_prefill_hinted(float* out, const void* q, const int32_t* q_start,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, int32_t bt_stride,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q,
+                                 int32_t max_q_len, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t num_pages, int32_t page_size,
+                                 int32_t window, int32_t hints, int32_t max_context_len,
+                                 float scale, int32_t dtype, void* workspace,
+                                 size_t* workspace_bytes, void* stream) {
+  return prefill_entry(out, q, q_start, k_pool, v_pool, block_tables, bt_stride, context_lens,
+                       num_seqs, num_q, max_q_len, q_heads, kv_heads, head_dim, num_pages,
+                       page_size, window, hints, max_context_len, scale, dtype, workspace,
+                       workspace_bytes, stream);
 }
 
 extern "C" int pa_reset_workspace(void* workspace, size_t workspace_bytes, void* stream) {

@@ -218,18 +218,22 @@ def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, *, out: torch.
 
 def _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
                   window, scale, max_context_len, ws_ptr, ws_size, stream_handle,
-                  layout="token"):
+                  layout="token", hints=0):
     n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
     num_q, hq, _ = (int(x) for x in q.shape)
     B = int(context_lens.shape[0])
     lib = _lib.load()
     size = ctypes.c_size_t(ws_size)
-    _lib.check("pa_prefill", lib.pa_prefill(
-        out.data_ptr() if out is not None else None, q.data_ptr(), q_start.data_ptr(),
-        k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
-        int(block_tables.shape[1]), context_lens.data_ptr(), B, num_q, int(max_q_len), hq, hkv,
-        d, n, P, int(window), int(max_context_len), float(scale), _fmt(q, layout), ws_ptr,
-        ctypes.byref(size), stream_handle))
+    head = (out.data_ptr() if out is not None else None, q.data_ptr(), q_start.data_ptr(),
+            k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+            int(block_tables.shape[1]), context_lens.data_ptr(), B, num_q, int(max_q_len), hq,
+            hkv, d, n, P, int(window))
+    tail = (int(max_context_len), float(scale), _fmt(q, layout), ws_ptr, ctypes.byref(size),
+            stream_handle)
+    if hints:
+        _lib.check("pa_prefill_hinted", lib.pa_prefill_hinted(*head, int(hints), *tail))
+    else:
+        _lib.check("pa_prefill", lib.pa_prefill(*head, *tail))
     return size.value
 
 
@@ -248,13 +252,14 @@ def prefill_workspace_bytes(q, q_start, k_pool, v_pool, block_tables, context_le
 def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len: int,
             window: int = 0, scale: Optional[float] = None, max_context_len: int = 0,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            stream=None, layout: str = "token") -> torch.Tensor:
+            stream=None, layout: str = "token", unshared_pages: bool = False) -> torch.Tensor:
     """Several query tokens per sequence (``pa_prefill``); returns fp32 ``[num_q, q_heads, head_dim]``.
 
     ``q`` is ``[num_q, q_heads, head_dim]``; the query rows of sequence ``s`` are
     ``q_start[s] .. q_start[s+1]-1`` (int32 ``[num_seqs + 1]``, at most
-    ``max_q_len`` per sequence) and are its last rows.  Workspace rules as for
-    ``decode``.
+    ``max_q_len`` per sequence) and are its last rows.  Workspace rules,
+    ``layout`` and ``unshared_pages`` (``pa_prefill_hinted``: same result bit for bit)
+    as for ``decode``.
     """
     dev = _dev(q, q_start, k_pool, v_pool, block_tables, context_lens)
     n, P, hkv, d = _pool_dims(k_pool, v_pool, layout)
@@ -285,7 +290,7 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, max_q_len
     _prefill_call(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, window,
                   scale, max_context_len, workspace.data_ptr(),
                   workspace.numel() * workspace.element_size(), _stream(dev, stream),
-                  layout=layout)
+                  layout=layout, hints=_lib.PA_HINT_UNSHARED if unshared_pages else 0)
     return out
 
 

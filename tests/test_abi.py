@@ -170,3 +170,22 @@ def test_head_major_flag_validation_needs_no_gpu():
     fake = ctypes.c_void_p(256)
     assert lib.pa_store_kv(fake, fake, fake, fake, fake, 1, 8, 16, 8, 1, _lib.PA_BF16 | HM,
                            None) == _lib.PA_EUNSUPPORTED
+
+
+def test_prefill_hints_validation_needs_no_gpu():
+    """pa_prefill_hinted takes PA_HINT_UNSHARED only, and sizes its workspace exactly as
+    pa_prefill does."""
+    lib = _lib.load()
+    size = ctypes.c_size_t(0)
+
+    def call(fn, *hint):
+        size.value = 0
+        rc = fn(None, None, None, None, None, None, 256, None, 4, 32, 8, 32, 8, 128, 1000, 16, 0,
+                *hint, 4096, 1.0, _lib.PA_BF16, None, ctypes.byref(size), None)
+        return rc, size.value
+
+    plain = call(lib.pa_prefill)
+    assert plain[0] == _lib.PA_OK and plain[1] > 0
+    assert call(lib.pa_prefill_hinted, _lib.PA_HINT_UNSHARED) == plain
+    assert call(lib.pa_prefill_hinted, 0) == plain
+    assert call(lib.pa_prefill_hinted, 2)[0] == _lib.PA_EINVAL

@@ -126,6 +126,30 @@ def test_unshared_hint_is_bit_identical(cfg, sinks):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("cfg,q_len", [(2, 4), (3, 4), (5, 4), (2, 128)])
+def test_prefill_hint_is_bit_identical(cfg, q_len):
+    """pa_prefill_hinted with PA_HINT_UNSHARED gives pa_prefill's output bit for bit: the
+    streaming path with one block per group (batch-64), the aligned window split, groups
+    of two blocks over a raw slot table, and the tile kernel for long chunks (which
+    ignores the hint)."""
+    o = ops()
+    base = workloads.config_spec(cfg)
+    sc = workloads.make_config(cfg, device="cuda", q_lo=q_len, q_hi=q_len,
+                               name=f"{base.name}_q{q_len}")
+    s = sc.spec
+    print(f"case {s.name} seed {sc.seed}", flush=True)
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    kv, vv = decode_views(sc)
+    outs = []
+    for hint in (False, True, True):
+        outs.append(o.prefill(sc.q, sc.q_start, kv, vv, sc.block_tables, sc.context_lens,
+                              max_q_len=q_len, window=s.window, scale=sc.scale,
+                              max_context_len=sc.max_context_len, unshared_pages=hint))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_config_prefix_full():
     # every sequence of the prefix-shared workload: 243 copy-on-write copies, the store,
     # then decode over the 128 shared prefix pages and each private suffix
