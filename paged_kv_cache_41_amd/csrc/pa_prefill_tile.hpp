@@ -86,6 +86,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// P.V runs in fp16: P rounded to nearest (11 significant bits), V converted from bf16 when
+// it is staged into LDS (exact for every bf16 value in fp16's normal range, 2^-14 to 65504;
+// smaller ones keep an absolute error below 2^-25).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 x) {
+  return make_uint4(pack_f16(bf16_lo(x.x), bf16_hi(x.x)), pack_f16(bf16_lo(x.y), bf16_hi(x.y)),
+                    pack_f16(bf16_lo(x.z), bf16_hi(x.z)), pack_f16(bf16_lo(x.w), bf16_hi(x.w)));
+}
+
 #ifndef PTILE_LPT
 #define PTILE_LPT 1
 #endif
@@ -259,13 +274,13 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
     char* vd = lds_v[buf];
     *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (0 ^ hx))) = rk0;
     *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (1 ^ hx))) = rk1;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (0 ^ hx))) = rv0;
-    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (1 ^ hx))) = rv1;
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (0 ^ hx))) = bf16x8_to_f16(rv0);
+    *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (1 ^ hx))) = bf16x8_to_f16(rv1);
     if constexpr (UPT > 2) {
       *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (2 ^ hx))) = rk2;
       *reinterpret_cast<uint4*>(kd + lds_off(kk, part + TPR * (3 ^ hx))) = rk3;
-      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (2 ^ hx))) = rv2;
-      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (3 ^ hx))) = rv3;
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (2 ^ hx))) = bf16x8_to_f16(rv2);
+      *reinterpret_cast<uint4*>(vd + lds_off(kk, part + TPR * (3 ^ hx))) = bf16x8_to_f16(rv3);
     }
   };
 
@@ -355,13 +370,15 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
         }
       }
       const float ms = m_ref[cb] == -INFINITY ? 0.f : m_ref[cb];
-      // P.V over 32 keys per product (v_mfma_f32_16x16x32_bf16): the A operand of lane
+      // P.V over 32 keys per product (v_mfma_f32_16x16x32_f16): the A operand of lane
       // (col, grp) holds column col's probabilities of keys 4 grp + r of two 16-row blocks,
       // and the B operand the same keys' values (the two transposing reads of those
-      // blocks), so both sides take the keys in the same order
+      // blocks, fp16 in LDS), so both sides take the keys in the same order.  The running
+      // sum adds the probabilities as rounded to fp16, so each output row is an exact
+      // convex combination of value rows with the weights the products used.
 #pragma unroll
       for (int kp = 0; kp < NKB / 2; ++kp) {
-        uint32_t hw[4], lw[4];
+        uint32_t hw[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int kb = 2 * kp + h;
@@ -369,24 +386,22 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
 #pragma unroll
           // (a column past the tile's queries has zero queries and finite values
           // throughout, and its output row is never written)
-          for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms));
-            l_run[cb] += p[r];
+          for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms));
+          hw[2 * h] = pack_f16(p[0], p[1]);
+          hw[2 * h + 1] = pack_f16(p[2], p[3]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const f16x2 q2 = __builtin_bit_cast(f16x2, hw[2 * h + i]);
+            l_run[cb] += (float)q2[0] + (float)q2[1];
           }
-          hw[2 * h] = pack_bf16(p[0], p[1]);
-          hw[2 * h + 1] = pack_bf16(p[2], p[3]);
-          lw[2 * h] = pack_bf16(p[0] - bf16_lo(hw[2 * h]), p[1] - bf16_hi(hw[2 * h]));
-          lw[2 * h + 1] = pack_bf16(p[2] - bf16_lo(hw[2 * h + 1]), p[3] - bf16_hi(hw[2 * h + 1]));
         }
-        const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        const bf16x8 plo_ = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        const f16x8 pv = __builtin_bit_cast(f16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint2 v0 = __builtin_bit_cast(uint2, vb[2 * kp][e]);
           const uint2 v1 = __builtin_bit_cast(uint2, vb[2 * kp + 1][e]);
-          const bf16x8 bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-          oacc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, oacc[cb][e], 0, 0, 0);
-          oacc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo_, bv, oacc[cb][e], 0, 0, 0);
+          const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          oacc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, bv, oacc[cb][e], 0, 0, 0);
         }
       }
     }
