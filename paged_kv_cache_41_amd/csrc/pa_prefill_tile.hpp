@@ -284,12 +284,15 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
     }
   };
 
-  float m_ref[CB], l_run[CB];
+  // lsum[cb][r]: running sum of column 4 grp + r's probabilities (as rounded to fp16), on
+  // the matrix cores: P times a block of ones, in the layout of the accumulators
+  float m_ref[CB];
+  f32x4 lsum[CB];
   f32x4 oacc[CB][8];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     m_ref[cb] = -INFINITY;
-    l_run[cb] = 0.f;
+    lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 8; ++e) oacc[cb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -360,11 +363,11 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float mn = fmaxf(m_ref[cb], mt);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[cb] - mn);
-        l_run[cb] *= alpha;
         m_ref[cb] = mn;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ar = __shfl(alpha, 4 * grp + r, 64);
+          lsum[cb][r] *= ar;
 #pragma unroll
           for (int e = 0; e < 8; ++e) oacc[cb][e][r] *= ar;
         }
@@ -374,8 +377,9 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
       // (col, grp) holds column col's probabilities of keys 4 grp + r of two 16-row blocks,
       // and the B operand the same keys' values (the two transposing reads of those
       // blocks, fp16 in LDS), so both sides take the keys in the same order.  The running
-      // sum adds the probabilities as rounded to fp16, so each output row is an exact
-      // convex combination of value rows with the weights the products used.
+      // sum is the same product against ones: the probabilities as rounded to fp16, so
+      // each output row is an exact convex combination of value rows with the weights the
+      // products used.
 #pragma unroll
       for (int kp = 0; kp < NKB / 2; ++kp) {
         uint32_t hw[4];
@@ -389,13 +393,10 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
           for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.qscale, -ms));
           hw[2 * h] = pack_f16(p[0], p[1]);
           hw[2 * h + 1] = pack_f16(p[2], p[3]);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const f16x2 q2 = __builtin_bit_cast(f16x2, hw[2 * h + i]);
-            l_run[cb] += (float)q2[0] + (float)q2[1];
-          }
         }
         const f16x8 pv = __builtin_bit_cast(f16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+        lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, ones, lsum[cb], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint2 v0 = __builtin_bit_cast(uint2, vb[2 * kp][e]);
@@ -455,12 +456,9 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   // 16 e + col
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    float lt = l_run[cb];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(lt, 4 * grp + r, 64);
+      const float lr = lsum[cb][r];
       const int h = 16 * (CB * w + cb) + 4 * grp + r;
       if ((h >> lg) < nt) {
         const float inv = lr > 0.f ? 1.f / lr : 0.f;
