@@ -1,10 +1,12 @@
-"""Test glue: torch tensors to raw-bit NumPy arrays, and the oracle's view of a step."""
+"""Test glue: torch tensors to raw-bit NumPy arrays, the oracle's view of a step, and the
+random shapes of several query tokens per sequence."""
 from __future__ import annotations
 
 import numpy as np
 import torch
 
 import oracle
+import workloads
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -54,3 +56,26 @@ def expected_step(sc, seqs=None, k_pool_bits=None, v_pool_bits=None):
 
 def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().to(torch.float64).numpy()
+
+
+def random_multi_spec(seed):
+    # random shapes for several query tokens per sequence: every path (streaming groups of
+    # 1 or 2 blocks, the tile kernel, the per-row kernels) and the boundaries between them
+    r = np.random.default_rng(1000 + seed)
+    kvh = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 3, 4, 8, 16]))
+    d = int(r.choice([128, 128, 128, 64]))
+    B = int(r.choice([1, 3, 8, 24, 40]))
+    q_hi = int(r.choice([2, 5, 17, 40, 90, 150]))
+    dt = str(r.choice(["bf16", "bf16", "f32"]))
+    if seed >= 24:
+        # shapes the tile kernel takes (long chunks over many tiles)
+        kvh, g, d, dt = int(r.choice([4, 8])), int(r.choice([2, 4, 8, 16])), 128, "bf16"
+        B, q_hi = 64, int(r.integers(100, 220))
+    len_hi = int(r.integers(q_hi, q_hi + 500))
+    return workloads.Spec(name=f"rmulti{seed}", dtype=dt,
+                          num_seqs=B, q_heads=kvh * g, kv_heads=kvh, head_dim=d,
+                          page_size=int(r.choice([1, 4, 16, 32])),
+                          window=int(r.choice([0, 0, 1, 9, 33, 300])), len_lo=1, len_hi=len_hi,
+                          q_lo=1, q_hi=q_hi, spare=str(r.choice(["canary", "nan"])),
+                          pool_factor=1.5)

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import bits, expected_step
+from helpers import bits, expected_step, random_multi_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,8 @@ def _step(sc, kp, vp, layout, unshared):
     if sc.q_start is not None:
         out = o.prefill(sc.q, sc.q_start, kp, vp, sc.block_tables, sc.context_lens,
                         max_q_len=max(int(sc.nq.max()), 1), window=s.window, scale=sc.scale,
-                        max_context_len=sc.max_context_len, layout=layout)
+                        max_context_len=sc.max_context_len, layout=layout,
+                        unshared_pages=unshared)
     else:
         out = o.decode(sc.q, kp, vp, sc.block_tables, sc.context_lens, window=s.window,
                        sinks=s.sinks, scale=sc.scale, max_context_len=sc.max_context_len,
@@ -137,3 +138,23 @@ def test_head_major_page_size_one_is_the_same_bytes():
     assert np.array_equal(bits(kp).ravel(), bits(sc.k_pool).ravel())
     assert np.array_equal(bits(vp).ravel(), bits(sc.v_pool).ravel())
     assert np.array_equal(bits(out_h), bits(out_t))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_head_major_hinted(seed):
+    """Random decode shapes (even seeds) and random shapes of several query tokens (odd
+    seeds), every path: head-major pools read with the unshared-pages hint give the pools
+    and outputs of token-major pools read without it, bit for bit.  (A hint only sets a
+    cache policy, so it is given here whether or not pages are shared.)"""
+    spec = workloads.random_spec(seed) if seed % 2 == 0 else random_multi_spec(seed)
+    sc = workloads.build(spec, 3000 + seed, device="cuda")
+    print(f"case {spec.name} seed {sc.seed}", flush=True)
+    if sc.table_page_size != sc.spec.page_size:
+        pytest.skip("a raw slot table reads pools as pages of one row: token-major only")
+    hk = sc.k_pool.transpose(1, 2).contiguous()
+    hv = sc.v_pool.transpose(1, 2).contiguous()
+    out_t = _step(sc, sc.k_pool, sc.v_pool, "token", False)
+    out_h = _step(sc, hk, hv, "head", True)
+    assert np.array_equal(bits(hk.transpose(1, 2)), bits(sc.k_pool)), "K pools differ"
+    assert np.array_equal(bits(hv.transpose(1, 2)), bits(sc.v_pool)), "V pools differ"
+    assert np.array_equal(bits(out_h), bits(out_t)), "outputs differ"

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import bits, expected_step, ints
+from helpers import bits, expected_step, ints, random_multi_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -479,32 +479,9 @@ def test_random_small(seed):
     check_step(sc)
 
 
-def _random_multi_spec(seed):
-    # random shapes for several query tokens per sequence: every path (streaming groups of
-    # 1 or 2 blocks, the tile kernel, the per-row kernels) and the boundaries between them
-    r = np.random.default_rng(1000 + seed)
-    kvh = int(r.choice([1, 2, 4, 8]))
-    g = int(r.choice([1, 2, 3, 4, 8, 16]))
-    d = int(r.choice([128, 128, 128, 64]))
-    B = int(r.choice([1, 3, 8, 24, 40]))
-    q_hi = int(r.choice([2, 5, 17, 40, 90, 150]))
-    dt = str(r.choice(["bf16", "bf16", "f32"]))
-    if seed >= 24:
-        # shapes the tile kernel takes (long chunks over many tiles)
-        kvh, g, d, dt = int(r.choice([4, 8])), int(r.choice([2, 4, 8, 16])), 128, "bf16"
-        B, q_hi = 64, int(r.integers(100, 220))
-    len_hi = int(r.integers(q_hi, q_hi + 500))
-    return workloads.Spec(name=f"rmulti{seed}", dtype=dt,
-                          num_seqs=B, q_heads=kvh * g, kv_heads=kvh, head_dim=d,
-                          page_size=int(r.choice([1, 4, 16, 32])),
-                          window=int(r.choice([0, 0, 1, 9, 33, 300])), len_lo=1, len_hi=len_hi,
-                          q_lo=1, q_hi=q_hi, spare=str(r.choice(["canary", "nan"])),
-                          pool_factor=1.5)
-
-
 @pytest.mark.parametrize("seed", range(36))
 def test_random_prefill(seed):
-    spec = _random_multi_spec(seed)
+    spec = random_multi_spec(seed)
     sc = workloads.build(spec, 2000 + seed, device="cuda")
     if len(sc.q) > 1500:
         rng = np.random.default_rng(seed)
