@@ -14,9 +14,10 @@
 // unit.  Each wavefront reads the keys and values from LDS in matrix-core operand
 // layouts: scores with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 of head_dim, B = 16
 // columns' queries), base-2 online softmax with a lazily raised reference max, P.V with
-// v_mfma_f32_16x16x32_bf16 over 32 keys (P as bf16 high part plus bf16 remainder; the V
-// operand read with transposing LDS reads, ds_read_b64_tr_b16, which hand each lane one
-// head_dim column of four key rows).  Each column is masked to its own query's rows
+// v_mfma_f32_16x16x32_f16 over 32 keys (P rounded to fp16; V converted to fp16 when it is
+// staged into LDS and read back with transposing LDS reads, ds_read_b64_tr_b16, which hand
+// each lane one head_dim column of four key rows), and the running sums as the same product
+// against ones.  Each column is masked to its own query's rows
 // (causal, the window counted from its row); the blocks every column attends run in a
 // loop of their own without masks.  A workgroup covers its tile's whole key range, so
 // there is no split and nothing to merge; every key row loaded lies in [window start of
