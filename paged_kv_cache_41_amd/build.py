@@ -24,6 +24,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          # keep uniform-address atomics as written: the optimizer's rewrite reads the
          # result right after the atomic, which drains every load in flight
          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+         # matrix-core accumulators in the vector registers: no moves between the vector
+         # and accumulation register files around every product (the verify step with
+         # groups of two query blocks runs 7% faster; decode 0.5-1%)
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
