@@ -469,7 +469,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         st_wgb[g] = sq >= B ? T : Hkv * st_cum[sq] + h * (st_cum[sq + 1] - st_cum[sq]);
       }
       __syncthreads();
-      if (tid < NWG) atomicMax(&st_scan[0], st_wgb[tid + 1] - st_wgb[tid]);
+      for (int g = tid; g < NWG; g += 64 * NW) atomicMax(&st_scan[0], st_wgb[g + 1] - st_wgb[g]);
       __syncthreads();
       const int mean = (T + NWG - 1) / NWG;
       part_of.aligned = st_scan[0] <= mean + mean / 16;
