@@ -133,10 +133,12 @@ def unique_kv_bytes(sc) -> int:
     return len(seen) * rows_per * 2 * s.kv_heads * s.head_dim * elt
 
 
-# The files the decode call's kernel is compiled from, and its build flags.
+# The files the decode call's kernel is compiled from, the host code that sizes its
+# launch, and the build flags.
 DECODE_SOURCES = ("paged_kv_cache_41_amd/csrc/pa_decode_stream.hpp",
                   "paged_kv_cache_41_amd/csrc/pa_common.hpp",
                   "paged_kv_cache_41_amd/csrc/pa_decode_mfma.hpp",
+                  "paged_kv_cache_41_amd/csrc/pa_kernels.hip",
                   "include/pa.h", "paged_kv_cache_41_amd/build.py")
 
 
