@@ -341,6 +341,9 @@ template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false, bool ALIGN = fal
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   constexpr bool MULTI = NB > 0;
   constexpr int NBX = MULTI ? NB : 1;
+  // WGL: a cut segment whose pieces all lie in this workgroup's ranges hands its partials
+  // over in LDS (slots of 16 columns: one block of columns at most)
+  constexpr bool WGL = NB <= 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -478,9 +481,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   }
   const int R = part_of.R;
   const int kw = blockIdx.x * NW + w;
-  if (!part_of.aligned && kw >= R) return;
-  const int ta = part_of.start(kw);
-  const int n = part_of.start(kw + 1) - ta;
+  // With WGL every wavefront of the workgroup reaches the barrier ahead of the combines in
+  // LDS, so one without a range (more wavefronts than tiles) only skips the stream.
+  const bool has_range = part_of.aligned || kw < R;
+  if (!WGL && !has_range) return;
+  const int ta = has_range ? part_of.start(kw) : 0;
+  const int n = has_range ? part_of.start(kw + 1) - ta : 0;
 
   const int P = a.page_size;
   const int lp = 31 - __clz(P);
@@ -642,6 +648,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // last (slot 1); segment index s * Hkv + g and the ranges of its first and last piece
   bool cut0 = false, cut1 = false;
   int seg0 = 0, k1_0 = 0, k2_0 = 0, seg1 = 0, k1_1 = 0, k2_1 = 0;
+  // the pieces of a cut segment, ranges k1 .. k2, all lie in this workgroup (ranges
+  // NW blockIdx .. NW blockIdx + NW - 1): its partials go through LDS
+  auto in_workgroup = [&](int k1, int k2) {
+    return part_of.aligned || (WGL && k1 / NW == k2 / NW);
+  };
 
   auto begin_segment = [&](const Desc& d, const Tile& Tl) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
@@ -692,6 +703,14 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     // slot 0 (the range's first segment) or 1 (its last), stored at device scope (written
     // through to the point where every compute unit reads it)
     const size_t pi = (size_t)kw * 2 + (first_seg ? 0 : 1);
+    int k1 = 0, k2 = 0;
+    if (!complete) {
+      const int tiles = st_cum[d.s + 1] - st_cum[d.s];
+      const int seg_start = Hkv * st_cum[d.s] + d.g * tiles;
+      k1 = part_of.of(seg_start);
+      k2 = part_of.of(seg_start + tiles - 1);
+    }
+    const bool in_lds = in_workgroup(k1, k2);
 #pragma unroll
     for (int i = 0; i < NBX; ++i) {
       float lt = l_run[i];
@@ -714,9 +733,9 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
             o[1] = make_float4(ac[4][r] * inv, ac[5][r] * inv, ac[6][r] * inv, ac[7][r] * inv);
           }
         }
-      } else if (part_of.aligned) {
-        // aligned partition: the piece's partial stays in LDS for the workgroup's combine
-        // (one block of 16 columns: with ALIGN, NB is at most 1)
+      } else if (in_lds) {
+        // every piece of the segment lies in this workgroup: the partial stays in LDS for
+        // the workgroup's combine (one block of 16 columns: NB is at most 1 here)
         float* pl = st_part[w][first_seg ? 0 : 1];
         if (lane < C) {
           pl[2 * lane] = m_ref[i];
@@ -748,9 +767,6 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       }
     }
     if (!complete) {
-      const int tiles = st_cum[d.s + 1] - st_cum[d.s];
-      const int seg_start = Hkv * st_cum[d.s] + d.g * tiles;
-      const int k1 = part_of.of(seg_start), k2 = part_of.of(seg_start + tiles - 1);
       if (first_seg) {
         cut0 = true;
         seg0 = d.s * Hkv + d.g;
@@ -931,6 +947,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       ncols = st_nt[s] << lg;
     }
     const int cd = (sl % LPC) * (QPL * 4);
+    const bool in_lds = in_workgroup(k1, k2);
     for (int h = sl / LPC; h < ncols; h += CPP) {
       float M = -INFINITY, den = 0.f;
       float4 nm[QPL];
@@ -942,7 +959,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
         for (int b = 0; b < COMBINE_BATCH; ++b) {
           const int k = min(k0 + b, k2);
-          if (part_of.aligned) {
+          if (in_lds) {
             // the piece of wavefront k - NW blockIdx of this workgroup, from LDS
             const float* pl = st_part[k - (int)blockIdx.x * NW][k == k1 ? slot1 : 0];
             ml[b] = make_float2(pl[2 * h], pl[2 * h + 1]);
@@ -982,18 +999,23 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       for (int q = 0; q < QPL; ++q)
         o[q] = make_float4(nm[q].x * inv, nm[q].y * inv, nm[q].z * inv, nm[q].w * inv);
     }
-    if (sl == 0 && !part_of.aligned)
+    if (sl == 0 && !in_lds)
       __hip_atomic_store(a.ws_arrive + k1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  // ---- cut segments: the piece that arrives last combines them ---------------------------
-  // Each piece counts itself on the counter of the segment's first range once its partial
-  // is written; the one that completes the count reads every piece's partial, combines
-  // them in range order, and puts the counter back to zero for the next call.  Partials
-  // and counters move only through device-scope accesses (stores written through, loads
-  // that skip the caches of the compute unit and of its die), and the count is raised only
-  // after this wavefront's partial stores have completed (vmcnt reaches 0), so a
-  // wavefront that sees the full count reads complete partials.  No cache-wide write-back
-  // or invalidate is needed: nothing is exchanged through ordinary cached stores.
+  // ---- cut segments -----------------------------------------------------------------------
+  // A segment whose pieces all lie in this workgroup's ranges (always, with the aligned
+  // partition; with the flat one, when its ranges are among this workgroup's four) hands
+  // its partials over in LDS and is combined after a barrier by the wavefront holding its
+  // first piece.  A segment cut across workgroups is combined by the piece that arrives
+  // last: each piece counts itself on the counter of the segment's first range once its
+  // partial is written; the one that completes the count reads every piece's partial,
+  // combines them in range order, and puts the counter back to zero for the next call.
+  // Those partials and counters move only through device-scope accesses (stores written
+  // through, loads that skip the caches of the compute unit and of its die), and the count
+  // is raised only after this wavefront's partial stores have completed (vmcnt reaches 0),
+  // so a wavefront that sees the full count reads complete partials.  No cache-wide
+  // write-back or invalidate is needed: nothing is exchanged through ordinary cached
+  // stores.  Either way the pieces are combined in range order with the same arithmetic.
   if (part_of.aligned) {
     // every piece of a cut segment lies in this workgroup: after the barrier the wavefront
     // holding a segment's first piece combines it from LDS.  A workgroup with fewer tiles
@@ -1015,34 +1037,49 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     }
     return;
   }
-  if (!cut0 && !cut1) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);   // all counters: every store above has completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int arrived0 = 0, arrived1 = 0;
-  if (lane == 0) {
-    if (cut0)
-      arrived0 = __hip_atomic_fetch_add(a.ws_arrive + k1_0, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    if (cut1)
-      arrived1 = __hip_atomic_fetch_add(a.ws_arrive + k1_1, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-  }
-  arrived0 = __builtin_amdgcn_readlane(arrived0, 0);
-  arrived1 = __builtin_amdgcn_readlane(arrived1, 0);
-  const bool last0 = cut0 && arrived0 == k2_0 - k1_0;
-  const bool last1 = cut1 && arrived1 == k2_1 - k1_1;
-  if (!last0 && !last1) return;
-  if constexpr (!MULTI) {
-    if (last0 && last1) {
+  // segments cut across workgroups: through the device-scope counters and partials
+  const bool dev0 = cut0 && !in_workgroup(k1_0, k2_0), dev1 = cut1 && !in_workgroup(k1_1, k2_1);
+  if (dev0 || dev1) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);   // all counters: every store above has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int arrived0 = 0, arrived1 = 0;
+    if (lane == 0) {
+      if (dev0)
+        arrived0 = __hip_atomic_fetch_add(a.ws_arrive + k1_0, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      if (dev1)
+        arrived1 = __hip_atomic_fetch_add(a.ws_arrive + k1_1, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    }
+    arrived0 = __builtin_amdgcn_readlane(arrived0, 0);
+    arrived1 = __builtin_amdgcn_readlane(arrived1, 0);
+    const bool last0 = dev0 && arrived0 == k2_0 - k1_0;
+    const bool last1 = dev1 && arrived1 == k2_1 - k1_1;
+    if (!MULTI && last0 && last1) {
       const bool hi = lane >= 32;
       combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0, hi ? k1_1 : k1_0,
               hi ? k2_1 : k2_0);
-      return;
+    } else {
+      if (last0) combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
+      if (last1) combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
     }
   }
-  if (last0) combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
-  if (last1) combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
+  if constexpr (WGL) {
+    // segments whose pieces all lie in this workgroup: once every wavefront has left its
+    // stream (and written its pieces to LDS), the wavefront holding a segment's first piece
+    // combines it.  Every wavefront of the workgroup reaches this barrier.
+    __syncthreads();
+    const bool own0 = cut0 && !dev0 && k1_0 == kw, own1 = cut1 && !dev1 && k1_1 == kw;
+    if (!MULTI && own0 && own1) {
+      const bool hi = lane >= 32;
+      combine(std::integral_constant<int, 32>{}, lane & 31, hi ? seg1 : seg0,
+              hi ? k1_1 : k1_0, hi ? k2_1 : k2_0);
+    } else {
+      if (own0) combine(std::integral_constant<int, 64>{}, lane, seg0, k1_0, k2_0);
+      if (own1) combine(std::integral_constant<int, 64>{}, lane, seg1, k1_1, k2_1);
+    }
+  }
 }
 
 // Tiles of the whole list at most: max_live attended rows per sequence, of which `sinks`
