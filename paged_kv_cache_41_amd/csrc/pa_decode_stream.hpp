@@ -36,8 +36,10 @@
 // enough); the accumulators are fp32.  A segment that starts and ends inside one
 // wavefront writes its output directly; the first and last segment of a range may be
 // cut and are written as partial (max, sum, accumulator) to one of two slots of that
-// wavefront; the wavefront that finishes a cut segment's last piece combines its pieces in
-// a fixed order.
+// wavefront: in LDS when every piece lies in the wavefront's workgroup (the wavefront
+// holding the first piece combines them after a workgroup barrier), else in device
+// memory (the wavefront that finishes the segment's last piece to arrive combines them).
+// Either way the pieces are combined in range order with the same arithmetic.
 //
 // Several query tokens per sequence (MULTI, NB > 0): the score columns are NB blocks of
 // 16 / G consecutive query tokens times the G heads of the group, so a segment is (group
