@@ -220,6 +220,20 @@ __shared__ int st_p0[BMAX];
 __shared__ int st_nt[BMAX];
 __shared__ int st_lo[BMAX];
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts by 1, 2, 4 and 8 lanes
+// inside each row of 16 (lanes shifted in from outside the row add 0), then the last lane
+// of row 0 added to row 1 and of row 2 to row 3, then the last lane of row 1 (the total of
+// rows 0 and 1) added to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2, 3
+  return v;
+}
+
 // Exclusive prefix sum over LDS counts arr[0..n) by the whole workgroup; arr[n] = total.
 __device__ __forceinline__ void wg_exclusive_scan(int* arr, int n, int tid, int lane, int w) {
   const int per = (n + 64 * NW - 1) / (64 * NW);
@@ -228,12 +242,7 @@ __device__ __forceinline__ void wg_exclusive_scan(int* arr, int n, int tid, int 
     const int x = tid * per + i;
     if (x < n) local += arr[x];
   }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_inclusive_sum(local);
   if (lane == 63) st_scan[w] = incl;
   __syncthreads();
   int base = 0;
@@ -281,12 +290,18 @@ struct Front {
   }
   // position of flattened tile x
   __device__ __forceinline__ void locate(int x) {
-    int lo_s = 0, hi_s = B - 1;
-    while (lo_s < hi_s) {
-      const int mid = (lo_s + hi_s + 1) >> 1;
-      if (Hkv * st_cum[mid] <= x) lo_s = mid; else hi_s = mid - 1;
-    }
-    f.s = uni(lo_s);
+    // the last s with Hkv st_cum[s] <= x: st_cum does not decrease, so those s are 0 .. s*;
+    // the lanes count them among every step-th entry (step = ceil(B / 64)), then among the
+    // step entries from the chunk that holds s* (one LDS read and one ballot each)
+    const int lane = threadIdx.x & 63;
+    const int step = (B + 63) >> 6;
+    const int s1 = lane * step;
+    const int c1 = __popcll(__ballot(s1 < B && Hkv * st_cum[s1 < B ? s1 : 0] <= x));
+    const int cs = (c1 - 1) * step;
+    const int s2 = cs + lane;
+    const int c2 =
+        __popcll(__ballot(lane < step && s2 < B && Hkv * st_cum[s2 < B ? s2 : 0] <= x));
+    f.s = uni(cs + c2 - 1);
     seg_fields();
     const int within = x - Hkv * st_cum[f.s];
     f.g = uni(within / f.tiles);
@@ -424,13 +439,8 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         local += t;
       }
     }
-    // inclusive scan within the wavefront (shuffles), then the wavefront totals in LDS
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
+    // inclusive scan within the wavefront, then the wavefront totals in LDS
+    const int incl = wave_inclusive_sum(local);
     if (lane == 63) st_scan[w] = incl;
     __syncthreads();
     int base = 0;
@@ -468,8 +478,10 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     const int NWG = gridDim.x;
     if (NWG * NW == a.total_waves && NWG <= BMAX / 4 && T >= NWG) {
       if (tid == 0) st_scan[0] = 0;
+      const bool narrow = (int64_t)NWG * B * Hkv < ((int64_t)1 << 31);
       for (int g = tid; g <= NWG; g += 64 * NW) {
-        const int j = (int)((int64_t)g * B * Hkv / NWG);
+        const int j = narrow ? (int)((uint32_t)(g * B * Hkv) / (uint32_t)NWG)
+                             : (int)((int64_t)g * B * Hkv / NWG);
         const int sq = j / Hkv, h = j - sq * Hkv;
         st_wgb[g] = sq >= B ? T : Hkv * st_cum[sq] + h * (st_cum[sq + 1] - st_cum[sq]);
       }
