@@ -234,6 +234,18 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// Largest of a non-negative value over the 64 lanes of a wavefront, in every lane (the same
+// row shifts and broadcasts, with max for +).
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Exclusive prefix sum over LDS counts arr[0..n) by the whole workgroup; arr[n] = total.
 __device__ __forceinline__ void wg_exclusive_scan(int* arr, int n, int tid, int lane, int w) {
   const int per = (n + 64 * NW - 1) / (64 * NW);
@@ -477,7 +489,6 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     // with st_cum[s + 1] - st_cum[s] tiles.
     const int NWG = gridDim.x;
     if (NWG * NW == a.total_waves && NWG <= BMAX / 4 && T >= NWG) {
-      if (tid == 0) st_scan[0] = 0;
       const bool narrow = (int64_t)NWG * B * Hkv < ((int64_t)1 << 31);
       for (int g = tid; g <= NWG; g += 64 * NW) {
         const int j = narrow ? (int)((uint32_t)(g * B * Hkv) / (uint32_t)NWG)
@@ -486,10 +497,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
         st_wgb[g] = sq >= B ? T : Hkv * st_cum[sq] + h * (st_cum[sq + 1] - st_cum[sq]);
       }
       __syncthreads();
-      for (int g = tid; g < NWG; g += 64 * NW) atomicMax(&st_scan[0], st_wgb[g + 1] - st_wgb[g]);
-      __syncthreads();
+      // every wavefront finds the largest workgroup itself (the same value in all)
+      int big = 0;
+      for (int g = lane; g < NWG; g += 64) big = max(big, st_wgb[g + 1] - st_wgb[g]);
+      big = wave_max_nonneg(big);
       const int mean = (T + NWG - 1) / NWG;
-      part_of.aligned = st_scan[0] <= mean + mean / 16;
+      part_of.aligned = big <= mean + mean / 16;
       if (part_of.aligned) part_of.R = a.total_waves;
     }
   }
