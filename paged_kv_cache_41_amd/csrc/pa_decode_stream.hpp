@@ -212,6 +212,10 @@ struct Desc {
 __shared__ int st_cum[BMAX + 1];   // tiles of sequences before s (st_cum[B] = all)
 __shared__ int st_len[BMAX];       // clamped context length
 __shared__ int st_scan[NW];       // wavefront totals of the scan
+__shared__ int st_scan2[NW];      // ... of the second array scanned with it
+// MULTI: per sequence, its first group of query tokens and its first tile (prefix sums)
+__shared__ int st_bseq[BMAX + 1];
+__shared__ int st_tseq[BMAX + 1];
 // MULTI: per block of query tokens, its sequence, first query row, position of its first
 // query (negative when the sequence has more queries than rows), tokens and first key row
 __shared__ int st_seq[BMAX];
@@ -246,29 +250,45 @@ __device__ __forceinline__ int wave_max_nonneg(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Exclusive prefix sum over LDS counts arr[0..n) by the whole workgroup; arr[n] = total.
-__device__ __forceinline__ void wg_exclusive_scan(int* arr, int n, int tid, int lane, int w) {
+// Exclusive prefix sums over two LDS count arrays a1[0..n) and a2[0..n) by the whole
+// workgroup, in one pass (two barriers); a1[n] and a2[n] receive the totals.
+__device__ __forceinline__ void wg_exclusive_scan2(int* a1, int* a2, int n, int tid, int lane,
+                                                   int w) {
   const int per = (n + 64 * NW - 1) / (64 * NW);
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int x = tid * per + i;
-    if (x < n) local += arr[x];
-  }
-  const int incl = wave_inclusive_sum(local);
-  if (lane == 63) st_scan[w] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += st_scan[i];
-  int run = base + incl - local;
+  int l1 = 0, l2 = 0;
   for (int i = 0; i < per; ++i) {
     const int x = tid * per + i;
     if (x < n) {
-      const int t = arr[x];
-      arr[x] = run;
-      run += t;
+      l1 += a1[x];
+      l2 += a2[x];
     }
   }
-  if (tid == 64 * NW - 1) arr[n] = base + incl;
+  const int i1 = wave_inclusive_sum(l1), i2 = wave_inclusive_sum(l2);
+  if (lane == 63) {
+    st_scan[w] = i1;
+    st_scan2[w] = i2;
+  }
+  __syncthreads();
+  int b1 = 0, b2 = 0;
+  for (int i = 0; i < w; ++i) {
+    b1 += st_scan[i];
+    b2 += st_scan2[i];
+  }
+  int r1 = b1 + i1 - l1, r2 = b2 + i2 - l2;
+  for (int i = 0; i < per; ++i) {
+    const int x = tid * per + i;
+    if (x < n) {
+      const int t1 = a1[x], t2 = a2[x];
+      a1[x] = r1;
+      a2[x] = r2;
+      r1 += t1;
+      r2 += t2;
+    }
+  }
+  if (tid == 64 * NW - 1) {
+    a1[n] = b1 + i1;
+    a2[n] = b2 + i2;
+  }
   __syncthreads();
 }
 
@@ -385,47 +405,69 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   int B = a.num_seqs;                         // segments per kv head: sequences or groups
 
   if constexpr (MULTI) {
-    // ---- groups of NB x 16 / G query tokens: counts per sequence, prefix sum, group
-    // records, then tile counts per group and their prefix sum -------------------------
+    // ---- groups of NB x 16 / G query tokens.  One thread per sequence counts its groups
+    // and their tiles; one workgroup scan gives each sequence its first group and its
+    // first tile; the same thread then writes its groups' records and first tiles -------
     const int tpb = (16 >> lg) * NB;
-    for (int s = tid; s < B; s += 64 * NW) {
-      const int q0 = a.q_start[s];
-      int n = a.q_start[s + 1] - q0;
+    // sequence s: first query row, query count (clamped to the call's bounds), length
+    auto seq_fields = [&](int s, int& q0, int& n, int& L) {
+      q0 = a.q_start[s];
+      n = a.q_start[s + 1] - q0;
       if (q0 < 0 || q0 > a.num_q) n = 0;
       n = max(0, min(min(n, a.num_q - q0), a.max_q));
-      st_cum[s] = (n + tpb - 1) / tpb;
+      const int ctx = a.ctx[s];
+      L = ctx > 0 ? (ctx < a.max_ctx ? ctx : a.max_ctx) : 0;
+    };
+    // group b of such a sequence: its tokens, the position of its first query, one past
+    // the last query's row, the first row any of its queries attends, and its tiles
+    struct Group { int nt, p0, kend, lo, tiles; };
+    auto group = [&](int n, int L, int b) {
+      Group g;
+      g.nt = min(tpb, n - b * tpb);
+      g.p0 = L - n + b * tpb;
+      g.kend = max(g.p0 + g.nt, 0);
+      g.lo = a.window > 0 ? max(g.p0 + 1 - a.window, 0) : 0;
+      g.tiles = g.kend > 0 ? ((g.kend - 1) >> 4) - (g.lo >> 4) + 1 : 0;
+      return g;
+    };
+    int f_q0 = 0, f_n = 0, f_L = 0;   // of sequence tid, kept for the records
+    for (int s = tid; s < B; s += 64 * NW) {
+      int q0, n, L;
+      seq_fields(s, q0, n, L);
+      if (s == tid) {
+        f_q0 = q0;
+        f_n = n;
+        f_L = L;
+      }
+      const int nb = (n + tpb - 1) / tpb;
+      int tiles = 0;
+      for (int b = 0; b < nb; ++b) tiles += group(n, L, b).tiles;
+      st_bseq[s] = nb;
+      st_tseq[s] = tiles;
     }
     __syncthreads();
-    wg_exclusive_scan(st_cum, B, tid, lane, w);
-    const int VB = st_cum[B];
+    wg_exclusive_scan2(st_bseq, st_tseq, B, tid, lane, w);
+    const int VB = st_bseq[B];
     for (int s = tid; s < B; s += 64 * NW) {
-      const int base = st_cum[s], nb = st_cum[s + 1] - base;
-      const int q0 = a.q_start[s];
-      const int n = nb > 0 ? max(0, min(min(a.q_start[s + 1] - q0, a.num_q - q0), a.max_q)) : 0;
-      const int ctx = a.ctx[s];
-      const int L = ctx > 0 ? (ctx < a.max_ctx ? ctx : a.max_ctx) : 0;
+      int q0 = f_q0, n = f_n, L = f_L;
+      if (s != tid) seq_fields(s, q0, n, L);
+      const int base = st_bseq[s], nb = st_bseq[s + 1] - base;
+      int first = st_tseq[s];
       for (int b = 0; b < nb; ++b) {
         const int v = base + b;
-        const int nt = min(tpb, n - b * tpb);
-        const int p0 = L - n + b * tpb;          // position of the block's first query
-        const int kend = max(p0 + nt, 0);        // one past the last query's row
-        const int lo = a.window > 0 ? max(p0 + 1 - a.window, 0) : 0;
+        const Group g = group(n, L, b);
         st_seq[v] = s;
         st_q0[v] = q0 + b * tpb;
-        st_p0[v] = p0;
-        st_nt[v] = nt;
-        st_lo[v] = lo;
-        st_len[v] = kend;
+        st_p0[v] = g.p0;
+        st_nt[v] = g.nt;
+        st_lo[v] = g.lo;
+        st_len[v] = g.kend;
+        st_cum[v] = first;
+        first += g.tiles;
       }
     }
+    if (tid == 0) st_cum[VB] = st_tseq[B];
     __syncthreads();
-    // st_cum is read above by every thread before any rewrites it
-    for (int v = tid; v < VB; v += 64 * NW) {
-      const int kend = st_len[v], lo = st_lo[v];
-      st_cum[v] = kend > 0 ? ((kend - 1) >> 4) - (lo >> 4) + 1 : 0;
-    }
-    __syncthreads();
-    wg_exclusive_scan(st_cum, VB, tid, lane, w);
     B = VB;
     // query rows of groups with nothing to attend are zero
     for (int v = blockIdx.x; v < B; v += gridDim.x) {
