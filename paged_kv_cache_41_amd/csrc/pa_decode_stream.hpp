@@ -46,6 +46,13 @@
 // of query tokens, kv head) and covers the rows the group's first query may attend up to
 // its last query's own row; each column is masked to its own query's rows (causal, window
 // counted from that query), and the NB blocks share every K/V tile and V operand gather.
+//
+// Head sets (HQ > 1, one query token, pages under 16 rows): a tile holds the same 16 rows
+// of HQ consecutive kv heads, read with one set of per-lane table entries, and a segment is
+// (sequence, head set).  The scores of head h are its four products against a copy of the
+// query operand that keeps only head h's columns (zero elsewhere), all accumulated into
+// the one score tile; in P.V, head h's values meet a copy of P that keeps only the rows
+// (columns) of head h.  Everything else sees one head of HQ x G query heads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,10 +90,13 @@ constexpr int COMBINE_BATCH = 4;   // pieces whose partials are loaded together
                                // registers go to the query groups)
 #endif
 
+// A tile holds the rows of HQ kv heads (a head set); head h's K and V are in k[4 h + j]
+// and v[4 h + j].
+template <int HQ>
 struct Tile {
-  uint4 k[4];        // K: token (lane % 16), bytes [64 j + 16 (lane / 16), +16) of its
+  uint4 k[4 * HQ];   // K: token (lane % 16), bytes [64 j + 16 (lane / 16), +16) of its
                      // head row in k[j]
-  uint4 v[4];        // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
+  uint4 v[4 * HQ];   // V: token 4 (lane / 16) + j, bytes [16 (lane % 16), +16)
   uint4 q[4];        // query column lane % 16, the same bytes as k: loaded with the
                      // tile that opens a segment piece only (groups of more than one block
                      // read their queries at the segment start instead)
@@ -386,8 +396,13 @@ struct Front {
 // columns share every K/V tile a wavefront loads.
 // VNT: the V rows are loaded with the non-temporal cache hint (pages not shared, so no
 // reuse to keep); K keeps the default policy, since its four loads per row share lines.
-template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false, bool ALIGN = false>
+// HQ > 1 (one query token only): a tile holds the same rows of HQ consecutive kv heads, and
+// a segment is (sequence, head set); the host passes kv_heads / HQ sets of group x HQ query
+// heads each, so that everything but the loads and the products sees one wider head.
+template <int DEPTH, bool PAGE_TILES, int NB, bool VNT = false, bool ALIGN = false, int HQ = 1>
 __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
+  static_assert(HQ == 1 || NB == 0, "head sets with one query token only");
+  using Tile = pa::stream::Tile<HQ>;
   constexpr bool MULTI = NB > 0;
   constexpr int NBX = MULTI ? NB : 1;
   // WGL: a cut segment whose pieces all lie in this workgroup's ranges hands its partials
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_pool);
   const uint32_t row_bytes = (uint32_t)a.row_stride * 2;      // one token's row of a head
   const uint32_t head_bytes = (uint32_t)a.head_stride * 2;    // one kv head within a page
-  const uint32_t page_bytes = (uint32_t)Hkv * HD * 2 * (uint32_t)P;
+  const uint32_t page_bytes = (uint32_t)(Hkv * HQ) * HD * 2 * (uint32_t)P;
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -647,39 +662,54 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
       const uint32_t bits = ((1u << hi_off) - 1u) & (~((1u << lo_off) - 1u) | ((1u << sl_off) - 1u));
       Tl.valid = mapped ? bits : 0u;
       const uint64_t base = (uint64_t)(uint32_t)min(max(pg, 0), last_page) * page_bytes +
-                            (uint32_t)(ut0 & (P - 1)) * row_bytes + (uint32_t)ug * head_bytes;
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + k_lane_off);
+                            (uint32_t)(ut0 & (P - 1)) * row_bytes +
+                            (uint32_t)(ug * HQ) * head_bytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
-      const char* vb = vbase + base + v_lane_off;
-      if constexpr (VNT) {
+      for (int h = 0; h < HQ; ++h) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kbase + base + h * head_bytes + k_lane_off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          Tl.v[j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                                  reinterpret_cast<const i32x4*>(vb + j * row_bytes)));
-      } else {
+        for (int j = 0; j < 4; ++j) Tl.k[4 * h + j] = kp[4 * j];
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Tl.v[j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
+      for (int h = 0; h < HQ; ++h) {
+        const char* vb = vbase + base + h * head_bytes + v_lane_off;
+        if constexpr (VNT) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            Tl.v[4 * h + j] = __builtin_bit_cast(
+                uint4, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vb + j * row_bytes)));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            Tl.v[4 * h + j] = *reinterpret_cast<const uint4*>(vb + j * row_bytes);
+        }
       }
     } else {
     const int tk = t0 + col;
     Tl.valid = (uint32_t)(__ballot((tk < d.sl || tk >= d.lo) && tk < d.L && e.k >= 0 &&
                                    e.k <= last_page) & 0xffffull);
-    const uint32_t hoff = (uint32_t)d.g * head_bytes;
+    const uint32_t hoff = (uint32_t)(d.g * HQ) * head_bytes;
     const int tkc = tk < d.sl ? tk : min(max(tk, d.lo), d.L - 1);
-    const uint4* kp = row_addr(kbase, min(max(e.k, 0), last_page), tkc, hoff + grp * 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Tl.k[j] = kp[4 * j];
+    for (int h = 0; h < HQ; ++h) {
+      const uint4* kp =
+          row_addr(kbase, min(max(e.k, 0), last_page), tkc, hoff + h * head_bytes + grp * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Tl.k[4 * h + j] = kp[4 * j];
+    }
+#pragma unroll
+    for (int h = 0; h < HQ; ++h)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tr = t0 + 4 * grp + j;
       const int tv = tr < d.sl ? tr : min(max(tr, d.lo), d.L - 1);
-      const uint4* vp = row_addr(vbase, min(max(e.v[j], 0), last_page), tv, hoff + col * 16);
+      const uint4* vp = row_addr(vbase, min(max(e.v[j], 0), last_page), tv,
+                                 hoff + h * head_bytes + col * 16);
       if constexpr (VNT)
-        Tl.v[j] = __builtin_bit_cast(
+        Tl.v[4 * h + j] = __builtin_bit_cast(
             uint4, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vp)));
       else
-        Tl.v[j] = *vp;
+        Tl.v[4 * h + j] = *vp;
     }
     }
   };
@@ -692,6 +722,11 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   bf16x8 qb[NBX][4];
   float m_ref[NBX], l_run[NBX];
   f32x4 oacc[NBX][8];
+  // (HQ > 1) the query operand of head h of the set: the lane's column's query where that
+  // column is one of head h's, zero elsewhere, so that head h's products add nothing to
+  // the other heads' columns
+  bf16x8 qm[HQ > 1 ? HQ : 1][4];
+  const int hc = HQ > 1 ? col / (G / HQ) : 0;   // head of the set column col belongs to
   bool first_seg = true;     // the segment being computed is the first of the range
   bool started_here = false; // ... and its tile 0 lies in this range
   // this lane's score column of each block is in use; (MULTI) the rows its query may
@@ -750,6 +785,12 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     if constexpr (NB <= 1) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) qb[0][j] = as_bf16x8(cval[0] ? Tl.q[j] : zero);
+      if constexpr (HQ > 1) {
+#pragma unroll
+        for (int h = 0; h < HQ; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qm[h][j] = as_bf16x8(hc == h && cval[0] ? Tl.q[j] : zero);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NBX; ++i) {
@@ -862,10 +903,20 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NBX; ++i) {
       sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (HQ > 1) {
+        // head h's keys against the queries of head h's columns (zero in the others)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[j]), qb[i][j], sc[i], 0, 0,
-                                                        0);
+        for (int h = 0; h < HQ; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[4 * h + j]), qm[h][j],
+                                                            sc[i], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Tl.k[j]), qb[i][j], sc[i],
+                                                          0, 0, 0);
+      }
     }
     // a tile whose rows every column attends needs no masks (most tiles of long contexts)
     bool plain = valid == 0xffffu;
@@ -928,28 +979,39 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
     // Rows outside the attended range get probability 0, but their V may be anything
     // (rows of the last page past the sequence end are never written): replace them by
     // zeros, since 0 * NaN would poison the product.
-    uint4 vt[4] = {Tl.v[0], Tl.v[1], Tl.v[2], Tl.v[3]};
-    if (valid != 0xffffu) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (!((valid >> (4 * grp + j)) & 1)) vt[j] = make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
-    const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
-    const uint32_t v2[4] = {vt[2].x, vt[2].y, vt[2].z, vt[2].w};
-    const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
+    for (int h = 0; h < HQ; ++h) {
+      uint4 vt[4] = {Tl.v[4 * h], Tl.v[4 * h + 1], Tl.v[4 * h + 2], Tl.v[4 * h + 3]};
+      if (valid != 0xffffu) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // column 8 col + e of the four tokens: the B operand (k = token, n = column block),
-      // gathered once and used by every block
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
-      const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
-      const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
+        for (int j = 0; j < 4; ++j)
+          if (!((valid >> (4 * grp + j)) & 1)) vt[j] = make_uint4(0, 0, 0, 0);
+      }
+      const uint32_t v0[4] = {vt[0].x, vt[0].y, vt[0].z, vt[0].w};
+      const uint32_t v1[4] = {vt[1].x, vt[1].y, vt[1].z, vt[1].w};
+      const uint32_t v2[4] = {vt[2].x, vt[2].y, vt[2].z, vt[2].w};
+      const uint32_t v3[4] = {vt[3].x, vt[3].y, vt[3].z, vt[3].w};
+      // (HQ > 1) head h's values only for the rows of P (columns) that are head h's
+      bf16x4 ph[NBX], pl[NBX];
 #pragma unroll
       for (int i = 0; i < NBX; ++i) {
-        oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[i], bv, oacc[i][e], 0, 0, 0);
-        oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[i], bv, oacc[i][e], 0, 0, 0);
+        const bf16x4 z = {0, 0, 0, 0};
+        ph[i] = HQ == 1 || hc == h ? phi[i] : z;
+        pl[i] = HQ == 1 || hc == h ? plo[i] : z;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // column 8 col + e of the four tokens: the B operand (k = token, n = column block),
+        // gathered once and used by every block
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t b01 = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+        const uint32_t b23 = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
+        const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b01, b23));
+#pragma unroll
+        for (int i = 0; i < NBX; ++i) {
+          oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph[i], bv, oacc[i][e], 0, 0, 0);
+          oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[i], bv, oacc[i][e], 0, 0, 0);
+        }
       }
     }
     if (flags & (SEG_LAST | RANGE_LAST))
@@ -999,7 +1061,7 @@ __global__ __launch_bounds__(64 * NW) void decode_stream_kernel(DecodeArgs a) {
   // usually a few) takes 4 columns per pass, several query tokens (16 or 32 columns) 8.
   // A decode wavefront that combines both of its segments gives each one half of its
   // lanes, so that the loads of the two combines are in flight together.
-  constexpr int CPP = MULTI ? 8 : 4;
+  constexpr int CPP = MULTI || HQ > 1 ? 8 : 4;
   auto combine = [&](auto nl_c, int sl, int seg, int k1, int k2) {
     constexpr int NL = decltype(nl_c)::value;
     constexpr int LPC = NL / CPP;             // lanes per column
@@ -1207,40 +1269,63 @@ inline void carve_workspace(DecodeArgs& a, void* workspace, int cols) {
   a.ws_acc = a.ws_ml + slots * 2;
 }
 
-template <int NB, bool ALIGN>
+template <int NB, bool ALIGN, int HQ>
 inline void launch_variant(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
   constexpr int D = NB > 0 ? STREAM_MULTI_DEPTH : STREAM_DEPTH;
   const bool unshared = (a.hints & PA_HINT_UNSHARED) != 0;
-  if (a.page_size >= TILE && unshared)
-    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true, ALIGN>), grid, block, 0, st, a);
-  else if (a.page_size >= TILE)
-    hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, false, ALIGN>), grid, block, 0, st,
-                       a);
-  else if (unshared)
-    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, true, ALIGN>), grid, block, 0, st,
-                       a);
+  if constexpr (HQ == 1) {   // (head sets serve pages under 16 rows only)
+    if (a.page_size >= TILE) {
+      if (unshared)
+        hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, true, ALIGN, 1>), grid, block, 0,
+                           st, a);
+      else
+        hipLaunchKernelGGL((decode_stream_kernel<D, true, NB, false, ALIGN, 1>), grid, block, 0,
+                           st, a);
+      return;
+    }
+  }
+  if (unshared)
+    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, true, ALIGN, HQ>), grid, block, 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, false, ALIGN>), grid, block, 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_stream_kernel<D, false, NB, false, ALIGN, HQ>), grid, block, 0,
+                       st, a);
 }
 
 // Only a kernel built with ALIGN tries the aligned partition, so the others carry none of
 // its branches.  (Its LDS partials hold one block of 16 columns: NB at most 1.)
-template <int NB>
+template <int NB, int HQ>
 inline void launch_nb(const DecodeArgs& a, hipStream_t st, dim3 grid, dim3 block) {
   if (NB <= 1 && a.try_aligned)
-    launch_variant<NB, NB <= 1>(a, st, grid, block);
+    launch_variant<NB, NB <= 1, HQ>(a, st, grid, block);
   else
-    launch_variant<NB, false>(a, st, grid, block);
+    launch_variant<NB, false, HQ>(a, st, grid, block);
 }
 
-// nb = 0: one query token per sequence; 1 or 2: blocks per group of query tokens
-inline int launch(const DecodeArgs& a, hipStream_t st, int nb) {
+// Kv heads per tile of the one-token path.  With pages under 16 rows every lane reads the
+// table entries of its own rows for each tile, and a tile of four (or two) kv heads reads
+// them once for all of its heads, whose columns fill the 16 of a product together (group
+// x heads at most 16); 4-5% faster on the raw slot-table workload, at every group size
+// measured.  With pages of 16 rows or more (one scalar entry per tile) tiles of several
+// heads ran slower, so those keep one head.  The choice is the same in both pool layouts,
+// which therefore give the same bits.
+inline int head_set(int group, int kv_heads, int page_size) {
+  if (page_size >= TILE) return 1;
+  if (group * 4 <= 16 && kv_heads % 4 == 0) return 4;
+  return group * 2 <= 16 && kv_heads % 2 == 0 ? 2 : 1;
+}
+
+// nb = 0: one query token per sequence (hq kv heads per tile: 1, 2 or 4); 1 or 2: blocks
+// per group of query tokens
+inline int launch(const DecodeArgs& a, hipStream_t st, int nb, int hq = 1) {
   const dim3 grid((unsigned)(a.total_waves / NW)), block(64 * NW);
-  switch (nb) {
-    case 0: launch_nb<0>(a, st, grid, block); break;
-    case 1: launch_nb<1>(a, st, grid, block); break;
-    case 2: launch_nb<2>(a, st, grid, block); break;
+  if (nb != 0 && hq != 1) return -1;
+  switch (nb * 8 + hq) {
+    case 1: launch_nb<0, 1>(a, st, grid, block); break;
+    case 2: launch_nb<0, 2>(a, st, grid, block); break;
+    case 4: launch_nb<0, 4>(a, st, grid, block); break;
+    case 9: launch_nb<1, 1>(a, st, grid, block); break;
+    case 17: launch_nb<2, 1>(a, st, grid, block); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

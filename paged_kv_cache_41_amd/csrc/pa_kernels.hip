@@ -505,10 +505,14 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
   a.hints = hints;
   a.sinks = window > 0 ? sinks : 0;
   pool_strides(head_major, page_size, kv_heads, head_dim, a.row_stride, a.head_stride);
-  if (stream::eligible(dtype, head_dim, group, page_size, num_seqs, bt_stride, kv_heads,
+  // Streaming path over head sets: a tile may take the same rows of hq consecutive kv
+  // heads; the kernel then sees kv_heads / hq heads of group x hq query heads each.
+  const int hq = stream::head_set(group, kv_heads, page_size);
+  const int vkv = kv_heads / hq, vgroup = group * hq;
+  if (stream::eligible(dtype, head_dim, vgroup, page_size, num_seqs, bt_stride, vkv,
                        max_live, run_sinks)) {
     // balanced streaming path: wavefronts and chunks sized to the largest possible list
-    const int64_t tiles_max = stream::tiles_bound(num_seqs, kv_heads, max_live, run_sinks);
+    const int64_t tiles_max = stream::tiles_bound(num_seqs, vkv, max_live, run_sinks);
     // about 22 tiles per wavefront at least (so the start-up and the end of a range stay
     // small next to its stream), at most stream_waves_max
     int64_t waves = tiles_max / stream_tiles_per_wave;
@@ -519,14 +523,14 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
     // often about equal: a grid of ceil(segs / k) workgroups, k = ceil(segs / 256), gives
     // each workgroup k or k - 1 whole segments, which lets the kernel use its aligned
     // partition (pieces of a cut segment combined in LDS) when the segments are even
-    const int64_t segs = (int64_t)num_seqs * kv_heads;
+    const int64_t segs = (int64_t)num_seqs * vkv;
     if (window > 0 && window < max_context_len && segs >= 64) {
       const int64_t wg_max = stream_waves_max / stream::NW;
       const int64_t k = (segs + wg_max - 1) / wg_max;
       waves = stream::NW * ((segs + k - 1) / k);
       a.try_aligned = 1;
     }
-    const size_t need = stream::workspace_bytes((int)waves, group);
+    const size_t need = stream::workspace_bytes((int)waves, vgroup);
     if (!workspace) {
       *workspace_bytes = need;
       return PA_OK;
@@ -546,17 +550,17 @@ static int decode_entry(float* out, const void* q, const void* k_pool, const voi
     a.ctx = context_lens;
     a.num_seqs = num_seqs;
     a.q_heads = q_heads;
-    a.kv_heads = kv_heads;
-    a.group = group;
+    a.kv_heads = vkv;
+    a.group = vgroup;
     a.num_pages = num_pages;
     a.page_size = page_size;
     a.window = window > 0 ? window : 0;
     a.max_ctx = max_context_len;
     a.qscale = scale * 1.4426950408889634f;
     a.total_waves = (int)waves;
-    stream::carve_workspace(a, workspace, group);
-    return stream::launch(a, reinterpret_cast<hipStream_t>(stream), 0) == 0 ? PA_OK
-                                                                           : PA_ELAUNCH;
+    stream::carve_workspace(a, workspace, vgroup);
+    return stream::launch(a, reinterpret_cast<hipStream_t>(stream), 0, hq) == 0 ? PA_OK
+                                                                               : PA_ELAUNCH;
   }
   a.chunk = pick_chunk(max_live);
   const bool fast = mfma::eligible(dtype, head_dim, group, page_size);

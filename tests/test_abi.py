@@ -128,6 +128,33 @@ def test_every_workspace_size_includes_the_counter_header():
         assert size.value > _lib.PA_WORKSPACE_HEADER, (dtype, d)
 
 
+def test_head_sets_show_in_the_workspace_size():
+    """The one-token streaming path keeps one partial of group x hq columns per range end,
+    hq kv heads per tile: 1 with pages of 16 rows or more, else the largest of 4 and 2 with
+    group x hq <= 16 that divides kv_heads (1 if none).  64 sequences of up to 4096 rows
+    give 1024 ranges in every case below."""
+    lib = _lib.load()
+    size = ctypes.c_size_t(0)
+
+    def need(q_heads, kv_heads, page_size):
+        size.value = 0
+        rc = lib.pa_decode(None, None, None, None, None, 4096 // page_size, None, 64, q_heads,
+                           kv_heads, 128, 100000, page_size, 0, 4096, 1.0, _lib.PA_BF16, None,
+                           ctypes.byref(size), None)
+        assert rc == _lib.PA_OK
+        return size.value
+
+    def expect(cols):
+        return _lib.PA_WORKSPACE_HEADER + 1024 * 2 * cols * (2 + 128) * 4
+
+    assert need(32, 8, 16) == expect(4)      # group 4, one head per tile
+    assert need(32, 8, 4) == expect(16)      # four heads per tile
+    assert need(32, 8, 1) == expect(16)
+    assert need(64, 8, 8) == expect(16)      # group 8: pairs
+    assert need(12, 6, 2) == expect(4)       # group 2, six heads: pairs, 4 columns
+    assert need(12, 3, 4) == expect(4)       # three heads: no set divides them
+
+
 def test_head_major_flag_validation_needs_no_gpu():
     """PA_HEAD_MAJOR is accepted by every call that takes the pools; any other bit in the
     dtype argument is rejected; the workspace a decode or prefill needs does not depend

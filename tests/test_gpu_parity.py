@@ -259,6 +259,33 @@ def test_sinks(name):
     check_step(sc)
 
 
+# Pages under 16 rows: the one-token streaming path takes tiles of 4 or 2 kv heads (as
+# many as keep group x heads within 16 score columns and divide kv_heads), or of one head
+# where no such set exists.  Every sequence against the oracle.
+HEAD_SETS = {
+    "hs4_p1_nan": dict(_GQA, num_seqs=48, page_size=1, len_lo=1, len_hi=700, spare="nan"),
+    "hs4_p4_window_sinks": dict(_GQA, num_seqs=40, page_size=4, window=100, sinks=5, len_lo=1,
+                                len_hi=600, spare="nan"),
+    "hs4_g1_p4": dict(dtype="bf16", q_heads=8, kv_heads=8, head_dim=128, num_seqs=24,
+                      page_size=4, len_lo=1, len_hi=500, spare="nan"),
+    "hs2_g8_p8": dict(dtype="bf16", q_heads=64, kv_heads=8, head_dim=128, num_seqs=32,
+                      page_size=8, len_lo=1, len_hi=900, spare="nan"),
+    "hs2_kv6_p2": dict(dtype="bf16", q_heads=12, kv_heads=6, head_dim=128, num_seqs=20,
+                       page_size=2, len_lo=1, len_hi=400, spare="nan"),
+    "hs2_g8_slots_window": dict(dtype="bf16", q_heads=64, kv_heads=8, head_dim=128,
+                                num_seqs=24, page_size=16, slot_table=True, window=300,
+                                len_lo=1, len_hi=1500),
+    "hs1_kv3_p4": dict(dtype="bf16", q_heads=12, kv_heads=3, head_dim=128, num_seqs=20,
+                       page_size=4, len_lo=1, len_hi=400, spare="nan"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_SETS))
+def test_head_sets_small_pages(name):
+    sc = workloads.build(workloads.Spec(name=name, **HEAD_SETS[name]), 33, device="cuda")
+    check_step(sc)
+
+
 def test_sinks_batch_above_streaming_limit():
     # the chunked matrix-core path: sink chunks, then window chunks
     spec = workloads.Spec(name="sinks_b2100", dtype="bf16", num_seqs=2100, q_heads=16,
@@ -695,7 +722,11 @@ def test_block_table_equals_slot_table():
     b = o.decode(sc.q, sc.k_pool.view(-1, 1, 8, 128), sc.v_pool.view(-1, 1, 8, 128),
                  slots.contiguous(), sc.context_lens, scale=sc.scale)
     torch.cuda.synchronize()
-    assert float((a - b).abs().max()) <= 1e-6
+    # The two calls split the work differently (the slot table's pages of one row take
+    # tiles of four kv heads), so their probabilities are rounded against different running
+    # maxima: P keeps about 16 significant bits (a bf16 high part and a bf16 remainder), so
+    # outputs of magnitude under 1 may differ by a few 1e-6.
+    assert float((a - b).abs().max()) <= 1e-5
 
 
 def test_decode_loop_with_allocator():
