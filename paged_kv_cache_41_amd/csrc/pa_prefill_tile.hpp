@@ -107,6 +107,10 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 x) {
 #endif
 constexpr int LPT_MAX = 256;    // sequences ordered longest first (more: in index order)
 
+// OFF32: pools under 4 GiB with pages and page counts under 2^24 bytes and pages: K/V rows
+// are read through buffer resources with 32-bit offsets formed by 24-bit multiplies, in
+// place of 64-bit address arithmetic for every load.
+template <bool OFF32>
 __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
   __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
@@ -252,9 +256,34 @@ __global__ __launch_bounds__(256, PTILE_WG_PER_CU) void prefill_tile_kernel(Deco
   // (the rows travel in named registers: arrays or structs shared between the lambdas
   // and the loop stayed in scratch memory)
   uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
+  // (OFF32) the pools as buffer resources, and this lane's byte offsets of its pieces
+  // within a key row of its head
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.k_pool), 0, (int)((uint32_t)a.num_pages * page_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.v_pool), 0, (int)((uint32_t)a.num_pages * page_bytes), 0x00020000);
+  const uint32_t piece0 = (uint32_t)g * (uint32_t)a.head_stride * 2u + part * 16;
+  auto ld = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t o) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0));
+  };
   auto load = [&](int b, int e) __attribute__((always_inline)) {
     const int key = min(max(kt0 + b * KT + kk, lo), kend - 1);
     const int pg = min(max(e, 0), last_page);
+    if constexpr (OFF32) {
+      const uint32_t o = __umul24((uint32_t)pg, page_bytes) +
+                         __umul24((uint32_t)(key & (P - 1)), row_bytes) + piece0;
+      rk0 = ld(rsk, o + TPR * 16 * (0 ^ hx));
+      rk1 = ld(rsk, o + TPR * 16 * (1 ^ hx));
+      rv0 = ld(rsv, o + TPR * 16 * (0 ^ hx));
+      rv1 = ld(rsv, o + TPR * 16 * (1 ^ hx));
+      if constexpr (UPT > 2) {
+        rk2 = ld(rsk, o + TPR * 16 * (2 ^ hx));
+        rk3 = ld(rsk, o + TPR * 16 * (3 ^ hx));
+        rv2 = ld(rsv, o + TPR * 16 * (2 ^ hx));
+        rv3 = ld(rsv, o + TPR * 16 * (3 ^ hx));
+      }
+      return;
+    }
     const size_t off = (size_t)(uint32_t)pg * page_bytes + (size_t)(key & (P - 1)) * row_bytes +
                        part * 16;
     const uint4* kp = reinterpret_cast<const uint4*>(kbase + off);
@@ -491,7 +520,13 @@ inline bool eligible(int dtype, int head_dim, int group, int page_size, int num_
 
 inline int launch(const DecodeArgs& a, hipStream_t st) {
   const int64_t blocks = grid_size(a.num_seqs, a.kv_heads, a.group, a.max_q);
-  hipLaunchKernelGGL(prefill_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  const uint64_t page_bytes = (uint64_t)a.kv_heads * HD * 2 * (uint64_t)a.page_size;
+  const bool off32 = page_bytes < (1u << 24) && (uint64_t)a.num_pages < (1u << 24) &&
+                     (uint64_t)a.num_pages * page_bytes < ((uint64_t)1 << 32);
+  if (off32)
+    hipLaunchKernelGGL(prefill_tile_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(prefill_tile_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
