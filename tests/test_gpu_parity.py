@@ -729,6 +729,46 @@ def test_block_table_equals_slot_table():
     assert float((a - b).abs().max()) <= 1e-5
 
 
+@pytest.mark.parametrize("q_len", [1, 64])
+def test_pools_above_4gib(q_len):
+    """Pools of more than 2^32 bytes, read with 64-bit offsets: the pages of a scenario are
+    moved to the top of 4.3 GB pools (table entries shifted with them), so every K/V row
+    lies past 4 GiB; decode (streaming kernel) and 64-token chunks (tile kernel) match the
+    oracle of the scenario as built."""
+    o = ops()
+    spec = workloads.Spec(name=f"pool_4g_q{q_len}", dtype="bf16", num_seqs=32, q_heads=32,
+                          kv_heads=8, head_dim=128, page_size=16, len_lo=64, len_hi=700,
+                          q_lo=q_len, q_hi=q_len, spare="nan")
+    sc = workloads.build(spec, 78, device="cuda")
+    print(f"case {spec.name} seed {sc.seed}", flush=True)
+    kp0, vp0 = bits(sc.k_pool), bits(sc.v_pool)
+    _, _, ref = expected_step(sc, k_pool_bits=kp0, v_pool_bits=vp0)
+    o.copy_pages(sc.k_pool, sc.v_pool, sc.copy_src, sc.copy_dst)
+    o.store_kv(sc.k_pool, sc.v_pool, sc.k_new, sc.v_new, sc.slot_mapping)
+    page_bytes = 16 * 8 * 128 * 2
+    n = (1 << 32) // page_bytes + sc.pool_pages + 64
+    base = n - sc.pool_pages
+    big_k = torch.zeros((n, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    big_v = torch.zeros_like(big_k)
+    big_k[base:] = sc.k_pool
+    big_v[base:] = sc.v_pool
+    bt = torch.where(sc.block_tables >= 0, sc.block_tables + base, sc.block_tables)
+    assert base * page_bytes >= (1 << 32)
+    if sc.q_start is not None:
+        out = o.prefill(sc.q, sc.q_start, big_k, big_v, bt, sc.context_lens, max_q_len=q_len,
+                        scale=sc.scale, max_context_len=sc.max_context_len)
+    else:
+        out = o.decode(sc.q, big_k, big_v, bt, sc.context_lens, scale=sc.scale,
+                       max_context_len=sc.max_context_len)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    del big_k, big_v
+    torch.cuda.empty_cache()
+    err = float(np.max(np.abs(got - ref)))
+    assert np.isfinite(got).all()
+    assert err <= TOL["bf16"], f"max abs error {err:.3g}"
+
+
 def test_decode_loop_with_allocator():
     """Several decode steps driven by the host allocator: forks, copy-on-write,
     window trims; pools stay bit-identical to the oracle's, outputs within tolerance."""
