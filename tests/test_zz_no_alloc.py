@@ -55,6 +55,16 @@ def test_noalloc_matches_workspace_call_large_then_small():
     _both(workloads.make_config(2, device="cuda", num_seqs=5, name="gqa_b5"), False)
 
 
+def test_noalloc_head_sets_on_small_pages():
+    # pages of one row (a raw slot table, G = 8: tiles of two kv heads, 16-column
+    # partials), then pages of 4 rows at G = 4 (four heads per tile), on the same buffer
+    _both(workloads.make_config(5, device="cuda", num_seqs=48, len_hi=6000,
+                                name="slot_b48"), True)
+    _both(workloads.build(workloads.Spec(name="p4_b16", dtype="bf16", num_seqs=16, q_heads=32,
+                                         kv_heads=8, head_dim=128, page_size=4, len_lo=1,
+                                         len_hi=900, spare="nan"), 35, device="cuda"), False)
+
+
 def test_noalloc_other_paths_and_sinks():
     # the window workload with sinks (streaming), then the per-row fp32 path (its
     # partials start after the counter header), then the streaming path again
